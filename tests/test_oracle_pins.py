@@ -1,0 +1,269 @@
+"""Pins for the CPU oracle: each check ties the oracle to something other than
+itself -- closed forms, brute force, an independent library routine, or an
+invariant the method must satisfy -- so that a dropped term, a wrong sign or
+index, or a transposed operand in the oracle fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import qsa_oracle as O
+
+
+def rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# ---------------------------------------------------------------- formats
+
+def test_fp8_anchor_values():
+    # OCP E4M3: bias 7, max normal 448 = 1.75 * 2^8, min normal 2^-6, min subnormal 2^-9
+    v = O.fp8_e4m3_to_f64(np.array([0x7E, 0x08, 0x01, 0x07, 0x38, 0xB8, 0x00, 0x80, 0x77, 0xFE]))
+    assert v[0] == 448.0
+    assert v[1] == 2.0 ** -6
+    assert v[2] == 2.0 ** -9
+    assert v[3] == 7 * 2.0 ** -9
+    assert v[4] == 1.0 and v[5] == -1.0
+    assert v[6] == 0.0 and v[7] == 0.0 and math.copysign(1, v[7]) == -1
+    assert v[8] == 240.0  # E=14, M=7: 1.875 * 2^7
+    assert v[9] == -448.0
+    assert np.isnan(O.fp8_e4m3_to_f64(np.array([0x7F, 0xFF]))).all()
+
+
+def test_fp8_decode_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.fp8_e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    both_nan = np.isnan(ours) & np.isnan(ref)
+    assert (both_nan | (ours == ref)).all()
+    assert both_nan.sum() == 2
+
+
+def test_bf16_decode_matches_torch():
+    x = torch.randn(10000, dtype=torch.float32, generator=torch.Generator().manual_seed(0)) * 100
+    xb = x.to(torch.bfloat16)
+    bits = xb.view(torch.int16).numpy()
+    assert np.array_equal(O.bf16_bits_to_f64(bits), xb.to(torch.float64).numpy())
+
+
+# ---------------------------------------------------------------- compress + score
+
+def test_compress_then_score_equals_token_level_sum():
+    """score(C_j) must equal sum over the block's 4 tokens of q . k_t (plain loops)."""
+    r = rng(1)
+    D, L = 8, 37
+    keys = r.integers(-127, 128, (L, D)).astype(np.int8)
+    q = r.integers(-127, 128, D).astype(np.int8)
+    s = O.score_blocks(q, O.compress_keys(keys, L))
+    assert s.shape == (L // 4,)
+    for j in range(L // 4):
+        tot = 0
+        for t in range(4 * j, 4 * j + 4):
+            for i in range(D):
+                tot += int(q[i]) * int(keys[t][i])
+        assert tot == int(s[j])
+
+
+def test_compress_only_closed_blocks():
+    keys = np.ones((11, 4), dtype=np.int8)
+    c = O.compress_keys(keys, 11)
+    assert c.shape == (2, 4) and (c == 4).all()
+    assert O.compress_keys(keys, 3).shape == (0, 4)
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_score_extremes_fit_int32(D):
+    keys = np.full((8, D), 127, dtype=np.int8)
+    q = np.full(D, 127, dtype=np.int8)
+    s = O.score_blocks(q, O.compress_keys(keys, 8))
+    assert (s == D * 127 * 508).all()
+    assert D * 127 * 508 < 2 ** 31
+    s2 = O.score_blocks(-q, O.compress_keys(keys, 8))
+    assert (s2 == -D * 127 * 508).all()
+
+
+# ---------------------------------------------------------------- select
+
+@pytest.mark.parametrize("seed", range(6))
+def test_select_matches_bruteforce_with_ties(seed):
+    r = rng(100 + seed)
+    for nb in [0, 1, 5, 31, 32, 33, 200]:
+        for k in [1, 7, 32, 64]:
+            scores = r.integers(-3, 4, nb)  # tiny range => many ties
+            got = O.select_blocks(scores, k).tolist()
+            assert got == O.select_blocks_bruteforce(scores.tolist(), k)
+
+
+def test_select_all_tied_takes_lowest_indices():
+    keys = np.full((400, 16), 5, dtype=np.int8)
+    q = np.full(16, 3, dtype=np.int8)
+    got = O.index_topk_row(q, keys, 400, 32)
+    assert got.tolist() == list(range(32))
+
+
+def test_select_planted_set():
+    r = rng(7)
+    D, L, k = 16, 4 * 300, 20
+    keys = r.integers(-5, 6, (L, D)).astype(np.int8)
+    planted = np.sort(r.choice(300, k, replace=False))
+    for j in planted:
+        keys[4 * j:4 * j + 4, 0] = 100
+    q = np.zeros(D, dtype=np.int8)
+    q[0] = 127
+    got = O.index_topk_row(q, keys, L, k)
+    assert np.array_equal(got, planted)
+
+
+def test_select_short_rows_pad():
+    keys = np.ones((3, 8), dtype=np.int8)
+    assert (O.index_topk_row(np.ones(8, np.int8), keys, 3, 4) == -1).all()
+    keys = np.ones((9, 8), dtype=np.int8)
+    assert O.index_topk_row(np.ones(8, np.int8), keys, 9, 4).tolist() == [0, 1, -1, -1]
+
+
+# ---------------------------------------------------------------- attention
+
+def _dense_case(L, hq=4, hkv=2, d=32, seed=0, k=512):
+    r = rng(seed)
+    D = 16
+    keys = r.integers(-127, 128, (L, D)).astype(np.int8)
+    qi = r.integers(-127, 128, D).astype(np.int8)
+    q = torch.randn(1, hq, d, generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16)
+    K = torch.randn(L, hkv, d, generator=torch.Generator().manual_seed(seed + 1)).to(torch.bfloat16)
+    V = torch.randn(L, hkv, d, generator=torch.Generator().manual_seed(seed + 2)).to(torch.bfloat16)
+    # one contiguous page holding the whole context: cache [1, H_kv, page, d]
+    kc = K.permute(1, 0, 2).unsqueeze(0).contiguous().view(torch.int16).numpy()
+    vc = V.permute(1, 0, 2).unsqueeze(0).contiguous().view(torch.int16).numpy()
+    topk = O.index_topk_row(qi, keys, L, k)[None]
+    res = O.decode_rows(q=q.view(torch.int16).numpy(), q_per_sel=1, sel_req=np.array([0]),
+                        sel_seq_len=np.array([L]), row_seq_len=np.array([L]), topk=topk,
+                        block_table=np.array([[0]]), page_size=max(L, 1), k_cache=kc, v_cache=vc,
+                        kv_dtype="bf16", scale=1 / math.sqrt(d), num_splits=1)
+    return q, K, V, res
+
+
+@pytest.mark.parametrize("L", [1, 3, 4, 5, 100, 2047, 2048, 2051])
+def test_dense_equivalence_short_context(L):
+    """With <= 512 closed blocks everything is selected: QSA == dense attention."""
+    hq, hkv, d = 4, 2, 32
+    q, K, V, res = _dense_case(L, hq, hkv, d, seed=L)
+    qq = q.to(torch.float64).reshape(1, hq, 1, d)
+    KK = K.to(torch.float64).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None]
+    VV = V.to(torch.float64).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, KK, VV, scale=1 / math.sqrt(d))
+    np.testing.assert_allclose(res["out"][0], ref[0, :, 0].numpy(), atol=1e-12, rtol=0)
+    logits = (qq @ KK.transpose(-1, -2))[0, :, 0] / math.sqrt(d)
+    np.testing.assert_allclose(res["lse"][0], torch.logsumexp(logits, dim=-1).numpy(), atol=1e-12)
+
+
+def test_dense_breaks_when_context_exceeds_budget():
+    """Above 4k+3 tokens the selection drops blocks: out differs from dense."""
+    L, hq, hkv, d = 4 * 40 + 2, 2, 1, 16
+    q, K, V, res = _dense_case(L, hq, hkv, d, seed=3, k=8)
+    qq = q.to(torch.float64).reshape(1, hq, 1, d)
+    KK = K.to(torch.float64).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None]
+    VV = V.to(torch.float64).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, KK, VV, scale=1 / math.sqrt(d))
+    assert np.abs(res["out"][0] - ref[0, :, 0].numpy()).max() > 1e-3
+
+
+def test_closed_forms():
+    r = rng(5)
+    T, hq, hkv, d = 50, 4, 2, 8
+    q = r.standard_normal((hq, d))
+    V = r.standard_normal((T, hkv, d))
+    out, lse = O.attend(q, np.zeros((T, hkv, d)), V, 0.3)
+    np.testing.assert_allclose(lse, np.log(T), atol=1e-14)
+    for h in range(hq):
+        np.testing.assert_allclose(out[h], V[:, h // 2].mean(axis=0), atol=1e-14)
+    K = r.standard_normal((T, hkv, d))
+    out, _ = O.attend(q, K, np.full((T, hkv, d), 2.5), 0.3)
+    np.testing.assert_allclose(out, 2.5, atol=1e-13)
+    out, lse = O.attend(q, K[:0], V[:0], 0.3)
+    assert (out == 0).all() and np.isneginf(lse).all()
+
+
+def test_gqa_grouping_contiguous():
+    """Head h must read KV head h // G: give each KV head a distinct constant V."""
+    T, hq, hkv, d = 6, 8, 4, 4
+    r = rng(9)
+    V = np.zeros((T, hkv, d))
+    for g in range(hkv):
+        V[:, g, :] = g + 1
+    out, _ = O.attend(r.standard_normal((hq, d)), r.standard_normal((T, hkv, d)), V, 1.0)
+    np.testing.assert_allclose(out[:, 0], [1, 1, 2, 2, 3, 3, 4, 4], atol=1e-13)
+
+
+# ---------------------------------------------------------------- splits + merge
+
+def _row_inputs(L=700, k=64, seed=11):
+    r = rng(seed)
+    hq, hkv, d = 4, 2, 16
+    keys = r.integers(-127, 128, (L, 8)).astype(np.int8)
+    qi = r.integers(-127, 128, 8).astype(np.int8)
+    topk = O.index_topk_row(qi, keys, L, k)
+    q = r.standard_normal((hq, d))
+    K = r.standard_normal((L, hkv, d))
+    V = r.standard_normal((L, hkv, d))
+    return topk, q, K, V
+
+
+@pytest.mark.parametrize("L", [700, 701, 702, 703])
+def test_split_partition_covers_token_set(L):
+    topk, *_ = _row_inputs(L)
+    full = O.token_positions(topk, L, L)
+    for P in [1, 2, 3, 8, 64, 100]:
+        parts = O.split_token_positions(topk, L, L, P)
+        assert len(parts) == P
+        cat = np.concatenate(parts)
+        assert np.array_equal(cat, full)
+        for p in parts[:-1]:
+            assert p.shape[0] % 4 == 0  # block boundaries
+
+
+@pytest.mark.parametrize("L", [700, 703])
+def test_merge_invariant_to_partition(L):
+    topk, q, K, V = _row_inputs(L)
+    ref_o, ref_l = O.attend(q, K[O.token_positions(topk, L, L)], V[O.token_positions(topk, L, L)], 0.25)
+    for P in [1, 2, 8, 100]:
+        parts = O.split_token_positions(topk, L, L, P)
+        res = [O.attend(q, K[t], V[t], 0.25) for t in parts]
+        o, l = O.merge_partials(np.stack([x[0] for x in res]), np.stack([x[1] for x in res]))
+        np.testing.assert_allclose(o, ref_o, atol=1e-12)
+        np.testing.assert_allclose(l, ref_l, atol=1e-12)
+    # position-owned partitions (how context-parallel ranks own slices), incl. empty ones
+    toks = O.token_positions(topk, L, L)
+    bounds = [0, 0, L // 3, L // 3, L // 2, L, L]
+    parts = [toks[(toks >= a) & (toks < b)] for a, b in zip(bounds[:-1], bounds[1:])]
+    assert any(p.shape[0] == 0 for p in parts)
+    res = [O.attend(q, K[t], V[t], 0.25) for t in parts]
+    o, l = O.merge_partials(np.stack([x[0] for x in res]), np.stack([x[1] for x in res]))
+    np.testing.assert_allclose(o, ref_o, atol=1e-12)
+    np.testing.assert_allclose(l, ref_l, atol=1e-12)
+
+
+def test_merge_all_empty():
+    o, l = O.merge_partials(np.zeros((3, 2, 4)), np.full((3, 2), -np.inf))
+    assert (o == 0).all() and np.isneginf(l).all()
+
+
+def test_merge_two_halves_closed_form():
+    """Two partials with equal lse average their outputs; lse grows by ln 2."""
+    o = np.stack([np.full((1, 3), 1.0), np.full((1, 3), 3.0)])
+    l = np.array([[0.7], [0.7]])
+    out, lse = O.merge_partials(o, l)
+    np.testing.assert_allclose(out, 2.0)
+    np.testing.assert_allclose(lse, 0.7 + math.log(2))
+
+
+# ---------------------------------------------------------------- reuse rows
+
+def test_reuse_rows_attend_selection_plus_own_tail():
+    sel_L, rows = 1000, [1000, 1001, 1002, 1003]
+    topk = np.arange(0, 64, dtype=np.int32) * 3
+    for L in rows:
+        t = O.token_positions(topk, sel_L, L)
+        assert t.shape[0] == 64 * 4 + (L - 1000)
+        assert (t[64 * 4:] == np.arange(1000, L)).all()
