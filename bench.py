@@ -1,0 +1,260 @@
+"""Benchmark of the QSA decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config 3] [--splits P] [--layers 12]
+
+A step is one decode step of every layer in a stack of `--layers` independent
+QSA layers (default 12, the number of QSA layers in the 48-layer model the
+pages describe), each layer running the whole hot path on its own caches:
+
+    qsa_compress -> qsa_index_topk -> qsa_sparse_decode -> qsa_merge_partials
+
+The per-layer caches (about 84 MB touched per layer at 256k context) rotate so
+that one step touches about 1 GB, far beyond the 256 MB Infinity Cache.  The
+step is captured once in a HIP graph and replayed; timing uses HIP events on
+the capture stream.  Inputs are seeded synthetic data resident in HBM.
+
+Printed: one JSON line with the throughput in query rows per second, the
+roofline of the dominant kernel (the compressed-key scan of qsa_index_topk,
+timed with HIP events around its own launches) and the CPU oracle's rate on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "QSA decode query-rows/s at 256k ctx; achieved HBM GB/s vs MI355X peak"
+HBM_PEAK_GBS = 8000.0
+BENCH_SPLITS = {1: 1, 2: 4, 3: 16, 4: 2, 5: 32}
+DESCR = {
+    1: "tiny: B=1, H 4/1, d=64, L=1,024, top-32 blocks, D=32, contiguous cache, bf16 K/V",
+    2: "decode-32k: B=32, H 16/2, d=128, L=32,768, top-512 blocks, D=64, 64-token pages, bf16 K/V",
+    3: "long-256k: B=8, H 16/2, d=128, L=262,144 (65,536 micro-blocks), top-512 blocks, D=64, "
+       "64-token shuffled pages, bf16 K/V",
+    4: "mixed-128: 128 requests, L log-uniform in [512, 262,144], H 16/2, d=128, top-512, bf16 K/V",
+    5: "fp8-1m: B=4, L=1,000,000, 4 query rows per request sharing one selection, fp8 E4M3 K/V",
+}
+
+
+def algorithmic_bytes(wl):
+    """Bytes the step must move, per layer (intermediates excluded).
+
+    scan: every closed micro-block of every selecting row at its stored width
+    (2 bytes per index dim), its page-table entries and the indexer query;
+    attend: the selected and tail K/V rows of each selecting row's request,
+    read once per KV head for all rows sharing the selection (+ fp8 scales),
+    q, the output (fp32) and lse.
+    """
+    s = wl.shape
+    D, page, d, hkv, hq = s.index_dim, s.page_size, s.head_dim, s.num_kv_heads, s.num_q_heads
+    esz = 1 if s.kv_dtype == "fp8" else 2
+    sel_len = wl.sel_seq_len.cpu().numpy().astype(np.int64)
+    row_len = wl.row_seq_len.cpu().numpy().astype(np.int64)
+    nb = sel_len // 4
+    scan = int((nb * 2 * D).sum() + (((sel_len + page - 1) // page) * 4).sum() + len(sel_len) * D)
+    attend = 0
+    for si in range(wl.num_sel):
+        rows = row_len[si * wl.q_per_sel:(si + 1) * wl.q_per_sel]
+        ntok = 4 * min(s.topk_blocks, int(nb[si])) + max(0, int(rows.max()) - 4 * int(nb[si]))
+        attend += ntok * hkv * d * esz * 2 + (ntok * 4 * 2 if s.kv_dtype == "fp8" else 0)
+    R = wl.num_rows
+    attend += R * hq * d * 2 + R * hq * d * 4 + R * hq * 4
+    return scan, attend
+
+
+def cpu_baseline(wl, seconds: float):
+    """Time the CPU oracle (as written, one thread) on rows of layer 0."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import qsa_oracle as O
+    from tests.harness import host_copy
+    h = host_copy(wl)
+    k = wl.shape.topk_blocks
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            for s in range(wl.num_sel):
+                b = int(h.sel_req[s])
+                L = int(h.sel_seq_len[s])
+                topk = np.full((wl.num_sel, k), -1, dtype=np.int32)
+                topk[s] = O.index_topk_row(h.q_index[s], h.keys[h.key_off[b]:h.key_off[b] + L], L, k)
+                rows = range(s * wl.q_per_sel, (s + 1) * wl.q_per_sel)
+                O.decode_rows(q=h.q, q_per_sel=wl.q_per_sel, sel_req=h.sel_req, sel_seq_len=h.sel_seq_len,
+                              row_seq_len=h.row_seq_len, topk=topk, block_table=h.block_table,
+                              page_size=wl.shape.page_size, k_cache=h.k_cache, v_cache=h.v_cache,
+                              kv_dtype=wl.shape.kv_dtype, scale=wl.shape.softmax_scale, num_splits=1,
+                              k_scale=h.k_scale, v_scale=h.v_scale, rows=rows)
+                done += wl.q_per_sel
+                if time.perf_counter() - t0 >= seconds:
+                    el = time.perf_counter() - t0
+                    return {"value": done / el, "unit": "query-rows/s", "cores": 1, "kind": "oracle",
+                            "sample": f"{done} query rows of layer 0 ({wl.name}), each: compress + score + "
+                                      f"select over the full context, then attention + merge, numpy int64/"
+                                      f"float64, one thread, {el:.1f} s"}
+
+
+def copy_calibration(mib: int):
+    """A plain device copy of known size (for scaling rocprofv3 byte counters)."""
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=12)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--kernel-iters", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the one-GPU path only: this build has no multi-GPU mode "
+              "(context-parallel sharding is described in the design notes, not built). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_sparse_attention_qsa_amd import _lib, build
+    if not os.path.exists(_lib.LIB_PATH):
+        build.build()
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
+    from block_sparse_attention_qsa_amd import api
+    from block_sparse_attention_qsa_amd.pipeline import QSALayer
+    from block_sparse_attention_qsa_amd.workloads import named_workload
+
+    cfg = args.config
+    P = args.splits or BENCH_SPLITS[cfg]
+    dev = "cuda"
+    layers = []
+    for li in range(args.layers):
+        wl = named_workload(cfg, device=dev, seed=None if li == 0 else 1000 * cfg + li)
+        layer = QSALayer(wl, num_splits=P)
+        layer.prefill()
+        layers.append(layer)
+        print(f"[bench] layer {li} ready ({wl.name}, rows={wl.num_rows})", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wl0 = layers[0].wl
+    rows_per_step = sum(l.wl.num_rows for l in layers)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def step():
+        for layer in layers:
+            layer.step(stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(args.steps):
+            if graph is not None:
+                graph.replay()
+            else:
+                step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # Dominant kernel: the compressed-key scan (qsa_index_topk with topk=None runs
+    # only that kernel).  HIP events around each launch, on the launch stream.
+    durs = []
+    with torch.cuda.stream(stream):
+        for it in range(args.kernel_iters + 1):
+            for layer in layers:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                api.qsa_index_topk(layer.cfg, layer.wl.q_index, layer.wl.sel_req, layer.wl.sel_seq_len,
+                                   layer.wl.block_table, layer.ckey, None, layer.workspace,
+                                   layer.max_seq_len, stream=stream)
+                b.record(stream)
+                if it > 0:
+                    durs.append((a, b))
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in durs]))
+
+    scan_b, attend_b = zip(*[algorithmic_bytes(l.wl) for l in layers])
+    scan_per_launch = float(np.mean(scan_b))
+    step_bytes = float(sum(scan_b) + sum(attend_b))
+    achieved = scan_per_launch / (kern_ms * 1e-3) / 1e9
+    rows_s = rows_per_step / (ms * 1e-3)
+
+    res = {
+        "metric": METRIC,
+        "value": rows_s,
+        "unit": "query-rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl0.shape.kv_dtype == "bf16" else "fp8",
+        "data": "synthetic",
+        "config": {"workload": f"cfg{cfg} {DESCR[cfg]}", "layers_per_step": args.layers,
+                   "query_rows_per_layer": wl0.num_rows, "splits": P, "hip_graph": graph is not None,
+                   "index_arith": "int8 dot4 -> int32 (exact)", "attention_arith": "bf16 MFMA / fp32 softmax"},
+        "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
+                     "frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "wall_s": t_wall},
+        "roofline": {"kernel": "qsa::score_kernel (qsa_index_topk compressed-key scan)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": scan_per_launch, "avg_launch_us": kern_ms * 1e3,
+                     "launches_timed": len(durs)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl0, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+"""Python binding of libqsa.so: the four QSA decode calls on torch tensors.
+
+Argument marshalling only -- every step runs in the HIP kernels of libqsa.so.
+Tensors must be CUDA (HIP) tensors, contiguous, of the dtypes stated below;
+the calls enqueue on the current torch stream (or `stream`) and return
+without synchronising.  A non-OK status raises QSAError carrying the
+library's own message.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+QSAError_codes = {
+    _lib.QSA_ERR_INVALID_ARGUMENT: "INVALID_ARGUMENT",
+    _lib.QSA_ERR_UNSUPPORTED: "UNSUPPORTED",
+    _lib.QSA_ERR_WORKSPACE: "WORKSPACE",
+    _lib.QSA_ERR_HIP: "HIP",
+}
+
+
+class QSAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{QSAError_codes.get(status, status)}: {msg}")
+        self.status = status
+
+
+@dataclass(frozen=True)
+class QSAConfig:
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    index_dim: int
+    topk_blocks: int
+    page_size: int
+    max_pages_per_req: int
+    kv_dtype: str = "bf16"  # "bf16" | "fp8"
+    softmax_scale: float = 0.0  # 0 => 1/sqrt(head_dim)
+    compress_ratio: int = 4
+
+    def to_c(self) -> _lib.qsa_config:
+        scale = self.softmax_scale if self.softmax_scale > 0 else self.head_dim ** -0.5
+        dt = {"bf16": _lib.QSA_KV_BF16, "fp8": _lib.QSA_KV_FP8_E4M3}.get(self.kv_dtype, -1)
+        return _lib.qsa_config(self.num_q_heads, self.num_kv_heads, self.head_dim, self.index_dim,
+                               self.compress_ratio, self.topk_blocks, self.page_size,
+                               self.max_pages_per_req, dt, scale)
+
+
+def _check(st: int) -> None:
+    if st != _lib.QSA_OK:
+        lib = _lib.load()
+        raise QSAError(st, lib.qsa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dt(t: torch.Tensor, *dtypes) -> None:
+    if t.dtype not in dtypes:
+        raise TypeError(f"expected dtype in {dtypes}, got {t.dtype}")
+
+
+def ckey_cache_bytes(cfg: QSAConfig, num_pages: int) -> int:
+    c = cfg.to_c()
+    return int(_lib.load().qsa_ckey_cache_bytes(ctypes.byref(c), num_pages))
+
+
+def qsa_compress(cfg: QSAConfig, new_keys: torch.Tensor, new_cu: torch.Tensor,
+                 seq_len_before: torch.Tensor, block_table: torch.Tensor, ring: torch.Tensor,
+                 ckey_cache: torch.Tensor, max_new_tokens: int, stream=None) -> None:
+    """Append new_keys (int8 [T, D]) per request; close micro-blocks into ckey_cache."""
+    _dt(new_keys, torch.int8); _dt(ring, torch.int8); _dt(ckey_cache, torch.int8)
+    _dt(new_cu, torch.int32); _dt(seq_len_before, torch.int32); _dt(block_table, torch.int32)
+    c = cfg.to_c()
+    B = seq_len_before.shape[0]
+    _check(_lib.load().qsa_compress(ctypes.byref(c), B, int(max_new_tokens), _ptr(new_keys),
+                                    _ptr(new_cu), _ptr(seq_len_before), _ptr(block_table),
+                                    _ptr(ring), _ptr(ckey_cache), _stream(stream)))
+
+
+def qsa_index_topk_workspace_size(cfg: QSAConfig, num_sel_rows: int, max_seq_len: int) -> int:
+    c = cfg.to_c()
+    return int(_lib.load().qsa_index_topk_workspace_size(ctypes.byref(c), num_sel_rows, max_seq_len))
+
+
+def qsa_index_topk_workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    _check(_lib.load().qsa_index_topk_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                     _stream(stream)))
+
+
+def qsa_index_topk(cfg: QSAConfig, q_index: torch.Tensor, sel_req: torch.Tensor,
+                   sel_seq_len: torch.Tensor, block_table: torch.Tensor, ckey_cache: torch.Tensor,
+                   topk: torch.Tensor, workspace: torch.Tensor, max_seq_len: int, stream=None) -> None:
+    """Top-k micro-blocks per selecting row into topk (int32 [S, k], ascending, -1 padded).
+    topk=None scores only (scores stay in the workspace)."""
+    _dt(q_index, torch.int8); _dt(ckey_cache, torch.int8)
+    if topk is not None:
+        _dt(topk, torch.int32)
+    _dt(sel_req, torch.int32); _dt(sel_seq_len, torch.int32); _dt(block_table, torch.int32)
+    c = cfg.to_c()
+    S = sel_req.shape[0]
+    _check(_lib.load().qsa_index_topk(ctypes.byref(c), S, int(max_seq_len), _ptr(q_index), _ptr(sel_req),
+                                      _ptr(sel_seq_len), _ptr(block_table), _ptr(ckey_cache),
+                                      _ptr(topk), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def qsa_sparse_decode(cfg: QSAConfig, q: torch.Tensor, row_seq_len: torch.Tensor,
+                      sel_req: torch.Tensor, sel_seq_len: torch.Tensor, topk: torch.Tensor,
+                      block_table: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      o_part: torch.Tensor, lse_part: torch.Tensor, q_per_sel: int = 1,
+                      k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    """Split partials of sparse attention: o_part fp32 [P, R, H_q, d], lse_part fp32 [P, R, H_q]."""
+    _dt(q, torch.bfloat16); _dt(o_part, torch.float32); _dt(lse_part, torch.float32)
+    _dt(row_seq_len, torch.int32); _dt(sel_req, torch.int32); _dt(sel_seq_len, torch.int32)
+    _dt(topk, torch.int32); _dt(block_table, torch.int32)
+    c = cfg.to_c()
+    S = sel_req.shape[0]
+    P = o_part.shape[0]
+    _check(_lib.load().qsa_sparse_decode(ctypes.byref(c), S, int(q_per_sel), P, _ptr(q), _ptr(row_seq_len),
+                                         _ptr(sel_req), _ptr(sel_seq_len), _ptr(topk), _ptr(block_table),
+                                         _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                         _ptr(o_part), _ptr(lse_part), _stream(stream)))
+
+
+def qsa_merge_partials(o_part: torch.Tensor, lse_part: torch.Tensor, out: torch.Tensor,
+                       lse: torch.Tensor, stream=None) -> None:
+    """LSE merge: out fp32 or bf16 [R, H, d] (by out's dtype), lse fp32 [R, H]."""
+    _dt(o_part, torch.float32); _dt(lse_part, torch.float32); _dt(out, torch.float32, torch.bfloat16)
+    _dt(lse, torch.float32)
+    P, R, H, d = o_part.shape
+    od = _lib.QSA_OUT_BF16 if out.dtype == torch.bfloat16 else _lib.QSA_OUT_F32
+    _check(_lib.load().qsa_merge_partials(P, R, H, d, _ptr(o_part), _ptr(lse_part), _ptr(out), od, _ptr(lse),
+                                          _stream(stream)))

@@ -1,0 +1,206 @@
+// Host entry points of libqsa.so: argument validation, then kernel launches.
+// Every check runs before anything is enqueued; see include/qsa.h for the
+// contract of each call.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "qsa.h"
+#include "qsa_internal.h"
+
+namespace qsa {
+
+static thread_local char g_err[512];
+
+qsa_status fail(qsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+qsa_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return QSA_OK;
+}
+
+static bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape checks common to the calls that take a qsa_config.
+static qsa_status check_config(const qsa_config* c, bool need_index, bool need_attn) {
+  if (!c) return fail(QSA_ERR_INVALID_ARGUMENT, "cfg is NULL");
+  if (c->compress_ratio != 4)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "compress_ratio must be 4 (got %d)", c->compress_ratio);
+  if (c->page_size < 16 || !is_pow2(c->page_size) || c->page_size % c->compress_ratio)
+    return fail(QSA_ERR_INVALID_ARGUMENT,
+                "page_size must be a power of two >= 16 divisible by the compress ratio (got %d)",
+                c->page_size);
+  if (c->max_pages_per_req < 1)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "max_pages_per_req must be >= 1 (got %d)", c->max_pages_per_req);
+  if (c->topk_blocks < 1 || c->topk_blocks > 2048)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "topk_blocks must be in [1, 2048] (got %d)", c->topk_blocks);
+  if (need_index) {
+    if (c->index_dim < 1)
+      return fail(QSA_ERR_INVALID_ARGUMENT, "index_dim must be positive (got %d)", c->index_dim);
+    if (c->index_dim != 32 && c->index_dim != 64 && c->index_dim != 128)
+      return fail(QSA_ERR_UNSUPPORTED, "index_dim %d not built (32, 64, 128)", c->index_dim);
+  }
+  if (need_attn) {
+    if (c->num_kv_heads < 1 || c->num_q_heads < 1 || c->num_q_heads % c->num_kv_heads)
+      return fail(QSA_ERR_INVALID_ARGUMENT, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                  c->num_q_heads, c->num_kv_heads);
+    if (c->num_kv_heads > 65535) return fail(QSA_ERR_INVALID_ARGUMENT, "num_kv_heads too large");
+    if (c->head_dim < 1) return fail(QSA_ERR_INVALID_ARGUMENT, "head_dim must be positive (got %d)", c->head_dim);
+    if (c->head_dim != 64 && c->head_dim != 128)
+      return fail(QSA_ERR_UNSUPPORTED, "head_dim %d not built (64, 128)", c->head_dim);
+    if (c->kv_dtype != QSA_KV_BF16 && c->kv_dtype != QSA_KV_FP8_E4M3)
+      return fail(QSA_ERR_UNSUPPORTED, "kv_dtype %d not supported", c->kv_dtype);
+    if (!(c->softmax_scale > 0.f) || c->softmax_scale > 1e30f)
+      return fail(QSA_ERR_INVALID_ARGUMENT, "softmax_scale must be positive and finite");
+  }
+  return QSA_OK;
+}
+
+}  // namespace qsa
+
+using namespace qsa;
+
+extern "C" {
+
+size_t qsa_ckey_cache_bytes(const qsa_config* cfg, int64_t num_pages) {
+  if (check_config(cfg, true, false) != QSA_OK || num_pages < 0) return 0;
+  return (size_t)num_pages * (size_t)cfg->page_size / 4 * 2 * (size_t)cfg->index_dim;
+}
+
+qsa_status qsa_compress(const qsa_config* cfg, int32_t num_reqs, int32_t max_new_tokens,
+                        const int8_t* new_keys, const int32_t* new_cu,
+                        const int32_t* seq_len_before, const int32_t* block_table,
+                        int8_t* ring, int8_t* ckey_cache, hipStream_t stream) {
+  qsa_status st = check_config(cfg, true, false);
+  if (st != QSA_OK) return st;
+  if (num_reqs < 0 || num_reqs > 65535)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "num_reqs must be in [0, 65535] (got %d)", num_reqs);
+  if (max_new_tokens < 0)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "max_new_tokens must be >= 0 (got %d)", max_new_tokens);
+  if (num_reqs == 0) return QSA_OK;
+  if (!new_cu || !seq_len_before || !block_table || !ring || !ckey_cache)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_compress: NULL array argument");
+  if (!new_keys && max_new_tokens > 0)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_compress: new_keys is NULL");
+  if (!aligned(ckey_cache, 16) || !aligned(ring, 4) || (new_keys && !aligned(new_keys, 4)))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_compress: ckey_cache needs 16-byte, ring/new_keys 4-byte alignment");
+  return launch_compress(*cfg, num_reqs, max_new_tokens, new_keys, new_cu, seq_len_before,
+                         block_table, ring, ckey_cache, stream);
+}
+
+size_t qsa_index_topk_workspace_size(const qsa_config* cfg, int32_t num_sel_rows, int32_t max_seq_len) {
+  if (check_config(cfg, true, false) != QSA_OK) return 0;
+  if (num_sel_rows < 0 || num_sel_rows > 65535 || max_seq_len < 0 || max_seq_len > QSA_MAX_SEQ_LEN) return 0;
+  return topk_workspace_layout(num_sel_rows, max_seq_len).total;
+}
+
+qsa_status qsa_index_topk_workspace_init(void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!workspace) return fail(QSA_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(QSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return launch_ws_clear(workspace, ws_bytes, stream);
+}
+
+qsa_status qsa_index_topk(const qsa_config* cfg, int32_t num_sel_rows, int32_t max_seq_len,
+                          const int8_t* q_index, const int32_t* sel_req,
+                          const int32_t* sel_seq_len, const int32_t* block_table,
+                          const int8_t* ckey_cache, int32_t* topk,
+                          void* workspace, size_t ws_bytes, hipStream_t stream) {
+  qsa_status st = check_config(cfg, true, false);
+  if (st != QSA_OK) return st;
+  if (num_sel_rows < 0 || num_sel_rows > 65535)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "num_sel_rows must be in [0, 65535] (got %d)", num_sel_rows);
+  if (max_seq_len < 0 || max_seq_len > QSA_MAX_SEQ_LEN)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "max_seq_len must be in [0, %d] (got %d)", QSA_MAX_SEQ_LEN, max_seq_len);
+  if (num_sel_rows == 0) return QSA_OK;
+  if (!q_index || !sel_req || !sel_seq_len || !block_table || !ckey_cache)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_index_topk: NULL array argument");
+  if (!aligned(ckey_cache, 16) || !aligned(q_index, 4))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_index_topk: ckey_cache needs 16-byte, q_index 4-byte alignment");
+  TopkWorkspace lay = topk_workspace_layout(num_sel_rows, max_seq_len);
+  if (!workspace) return fail(QSA_ERR_WORKSPACE, "qsa_index_topk: workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(QSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < lay.total)
+    return fail(QSA_ERR_WORKSPACE, "qsa_index_topk: workspace has %zu bytes, needs %zu", ws_bytes, lay.total);
+  return launch_index_topk(*cfg, num_sel_rows, max_seq_len, q_index, sel_req, sel_seq_len,
+                           block_table, ckey_cache, topk, lay, workspace, stream);
+}
+
+qsa_status qsa_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_t q_per_sel,
+                             int32_t num_splits, const void* q, const int32_t* row_seq_len,
+                             const int32_t* sel_req, const int32_t* sel_seq_len,
+                             const int32_t* topk, const int32_t* block_table,
+                             const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale,
+                             float* o_part, float* lse_part, hipStream_t stream) {
+  qsa_status st = check_config(cfg, false, true);
+  if (st != QSA_OK) return st;
+  if (num_sel_rows < 0 || num_sel_rows > 65535)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "num_sel_rows must be in [0, 65535] (got %d)", num_sel_rows);
+  if (num_splits < 1 || num_splits > 64)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "num_splits must be in [1, 64] (got %d)", num_splits);
+  if (q_per_sel < 1) return fail(QSA_ERR_INVALID_ARGUMENT, "q_per_sel must be >= 1 (got %d)", q_per_sel);
+  const int G = cfg->num_q_heads / cfg->num_kv_heads;
+  if ((int64_t)G * q_per_sel > 64)
+    return fail(QSA_ERR_UNSUPPORTED, "q_per_sel * (num_q_heads/num_kv_heads) = %lld exceeds 64",
+                (long long)G * q_per_sel);
+  if ((int64_t)num_sel_rows * q_per_sel > (1 << 24))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "too many query rows");
+  if (num_sel_rows == 0) return QSA_OK;
+  if (!q || !row_seq_len || !sel_req || !sel_seq_len || !topk || !block_table || !k_cache || !v_cache ||
+      !o_part || !lse_part)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_sparse_decode: NULL array argument");
+  if (cfg->kv_dtype == QSA_KV_FP8_E4M3 && (!k_scale || !v_scale))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_sparse_decode: fp8 K/V need k_scale and v_scale");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_sparse_decode: q, k_cache, v_cache need 16-byte alignment");
+  return launch_sparse_decode(*cfg, num_sel_rows, q_per_sel, num_splits, q, row_seq_len, sel_req,
+                              sel_seq_len, topk, block_table, k_cache, v_cache, k_scale, v_scale,
+                              o_part, lse_part, stream);
+}
+
+qsa_status qsa_merge_partials(int32_t num_splits, int32_t num_rows, int32_t num_heads,
+                              int32_t head_dim, const float* o_part, const float* lse_part,
+                              void* out, int32_t out_dtype, float* lse, hipStream_t stream) {
+  if (num_splits < 1 || num_splits > 64)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "num_splits must be in [1, 64] (got %d)", num_splits);
+  if (num_rows < 0 || num_heads < 1)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "num_rows must be >= 0 and num_heads >= 1");
+  if ((int64_t)num_rows * num_heads > (int64_t)1 << 30)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "num_rows * num_heads too large");
+  if (head_dim < 1) return fail(QSA_ERR_INVALID_ARGUMENT, "head_dim must be positive (got %d)", head_dim);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(QSA_ERR_UNSUPPORTED, "head_dim %d not built (64, 128)", head_dim);
+  if (out_dtype != QSA_OUT_F32 && out_dtype != QSA_OUT_BF16)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "out_dtype must be QSA_OUT_F32 or QSA_OUT_BF16 (got %d)", out_dtype);
+  if (num_rows == 0) return QSA_OK;
+  if (!o_part || !lse_part || !out || !lse)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_merge_partials: NULL array argument");
+  return launch_merge(num_splits, num_rows, num_heads, head_dim, o_part, lse_part, out,
+                      out_dtype == QSA_OUT_BF16, lse, stream);
+}
+
+const char* qsa_status_string(qsa_status s) {
+  switch (s) {
+    case QSA_OK: return "QSA_OK";
+    case QSA_ERR_INVALID_ARGUMENT: return "QSA_ERR_INVALID_ARGUMENT";
+    case QSA_ERR_UNSUPPORTED: return "QSA_ERR_UNSUPPORTED";
+    case QSA_ERR_WORKSPACE: return "QSA_ERR_WORKSPACE";
+    case QSA_ERR_HIP: return "QSA_ERR_HIP";
+  }
+  return "QSA_ERR_UNKNOWN";
+}
+
+const char* qsa_last_error(void) { return g_err; }
+
+const char* qsa_version(void) { return "qsa-mi355x 0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Host-side internals shared by the QSA translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qsa.h"
+
+namespace qsa {
+
+// Records a message for qsa_last_error() and returns `st`.
+qsa_status fail(qsa_status st, const char* fmt, ...);
+
+// Checks hipGetLastError() after a launch.
+qsa_status check_launch(const char* what);
+
+// Workspace layout of qsa_index_topk (offsets in bytes from the base).
+struct TopkWorkspace {
+  int32_t rows;        // selecting rows it is sized for
+  int32_t nb_stride;   // micro-block capacity per row (multiple of the chunk)
+  size_t off_scores;   // int32  [rows][nb_stride]
+  size_t off_keys;     // uint64 [rows][nb_stride]  candidates of the threshold bin
+  size_t off_bitmap;   // uint64 [rows][nb_stride/64]
+  size_t off_hist;     // uint32 [rows][kBins]
+  size_t off_ctr;      // uint32 [rows][4]: done1, done2, n_cand, pad
+  size_t off_meta;     // int32  [rows][2]: threshold bin, count strictly above it
+  size_t total;
+};
+
+constexpr int kScoreChunk = 1024;  // micro-blocks per scoring workgroup
+constexpr int kBins = 2048;        // histogram bins of the score's top bits
+constexpr int kBinShift = 14;      // bin = (score + 2^24) >> 14
+
+TopkWorkspace topk_workspace_layout(int32_t rows, int32_t max_seq_len);
+
+qsa_status launch_compress(const qsa_config& c, int32_t num_reqs, int32_t max_new_tokens,
+                           const int8_t* new_keys, const int32_t* new_cu,
+                           const int32_t* seq_len_before, const int32_t* block_table,
+                           int8_t* ring, int8_t* ckey, hipStream_t stream);
+
+qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len,
+                             const int8_t* q_index, const int32_t* sel_req,
+                             const int32_t* sel_seq_len, const int32_t* block_table,
+                             const int8_t* ckey, int32_t* topk, const TopkWorkspace& ws,
+                             void* ws_base, hipStream_t stream);
+
+qsa_status launch_ws_clear(void* ws, size_t bytes, hipStream_t stream);
+
+qsa_status launch_sparse_decode(const qsa_config& c, int32_t S, int32_t q_per_sel, int32_t P,
+                                const void* q, const int32_t* row_seq_len, const int32_t* sel_req,
+                                const int32_t* sel_seq_len, const int32_t* topk,
+                                const int32_t* block_table, const void* k_cache,
+                                const void* v_cache, const float* k_scale, const float* v_scale,
+                                float* o_part, float* lse_part, hipStream_t stream);
+
+qsa_status launch_merge(int32_t P, int32_t R, int32_t H, int32_t d, const float* o_part,
+                        const float* lse_part, void* out, bool out_bf16, float* lse, hipStream_t stream);
+
+}  // namespace qsa

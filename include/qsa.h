@@ -1,0 +1,225 @@
+/*
+ * qsa.h -- C ABI of libqsa.so, the MI355X (gfx950) decode path of QSA
+ * (Qwen Sparse Attention).
+ *
+ * Sources (web pages) cited below:
+ *   [QSA-DCP]  "Qwen 4 QSA 迎来解码上下文并行：深入解读 vLLM 针对 Qwen3.8-Flash-Next 的
+ *              草稿 PR" (orcarouter.ai blog), section "拉取请求实际改变了什么" (what the
+ *              pull request actually changes): a lightweight indexer compresses keys
+ *              into micro-blocks at ratio 4, scores them, keeps the best 512 blocks
+ *              (about 2,048 tokens) and runs the final softmax and value aggregation
+ *              over the uncompressed K/V at those positions; with decode context
+ *              parallelism each rank reads its own slice of the main KV cache and
+ *              the partial attention results are merged at the end; the selector
+ *              and the main KV cache live in one cache group so they cannot drift;
+ *              synthetic (dummy) batches must not write the indexer's side cache.
+ *   [PR53896]  "PR #53896 完整报告" (prhub.com.cn report on vLLM PR #53896), section
+ *              "实现拆解" (implementation breakdown): startup check that the compress
+ *              ratio divides the KV block size; the indexer writes token keys into a
+ *              raw-key ring and pools them by the compress ratio into a compressed
+ *              key cache, then does a weight-free top-k on the compressed keys.
+ *              Section "关键源码片段" (key source snippets), QSAIndexer: fixed-width
+ *              int32 output padded with -1; a paged KV cache is required; a later
+ *              MTP step may reuse the first step's selection.
+ *
+ * Conventions for every entry point
+ *   - All array arguments are DEVICE pointers to caller-owned memory.  The
+ *     library never allocates, frees or synchronises; every call only enqueues
+ *     kernels on `stream` (0 = the null stream) and returns.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     failed check returns a status and enqueues nothing.  QSA_ERR_HIP means a
+ *     launch failed (hipGetLastError after the launch); later kernels of the
+ *     same call are then not enqueued.  qsa_last_error() describes the last
+ *     failure on the calling thread.  No C++ exception crosses this ABI.
+ *   - Data-dependent contracts (page ids inside the pool, seq_len within the
+ *     block-table capacity, the bounds stated per call) are not checked on the
+ *     device; violating them is undefined behaviour.
+ *   - Calls that share a workspace, ring or output buffer must be ordered
+ *     (same stream, or synchronised); overlapping calls on them race.
+ *
+ * Layouts (all row-major, innermost last)
+ *   block_table  int32 [num_reqs, max_pages_per_req]: logical page -> physical page.
+ *                One table serves both the K/V cache and the compressed-key cache
+ *                ([QSA-DCP]: selector and main KV in one cache group).
+ *   K/V cache    [num_pages, H_kv, page_size, head_dim]; bf16, or fp8 E4M3 (OCP)
+ *                bytes with k_scale / v_scale fp32 [num_pages, page_size] (one
+ *                scale per token per tensor).  Token t of request b is at page
+ *                block_table[b][t / page_size], slot t % page_size.
+ *   ckey cache   int8 [num_pages, 2*D/16, page_size/4, 16]: micro-block j of a
+ *                request lives in page block_table[b][4j / page_size], slot
+ *                j % (page_size/4).  Its exact integer key C (sum of 4 int8 keys,
+ *                |C| <= 512) is stored losslessly in two int8 planes,
+ *                C = 256*hi + lo with lo = (int8)C and hi in [-2, 2]; chunk c < D/16
+ *                holds lo bytes of dims [16c, 16c+16), chunk D/16 + c the hi bytes.
+ *                Size: qsa_ckey_cache_bytes().
+ *   ring         int8 [num_reqs, 4, D]: the keys of each request's open micro-block
+ *                (slot t % 4).  Only slots of the open block are ever read.
+ */
+#ifndef QSA_H_
+#define QSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QSA_OK = 0,
+  QSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, ratio != 4, ...     */
+  QSA_ERR_UNSUPPORTED = 2,      /* valid but not built: head_dim, index_dim, ... */
+  QSA_ERR_WORKSPACE = 3,        /* workspace missing or too small               */
+  QSA_ERR_HIP = 4               /* a HIP launch failed                          */
+} qsa_status;
+
+typedef enum { QSA_KV_BF16 = 0, QSA_KV_FP8_E4M3 = 1 } qsa_kv_dtype;
+
+/* Static shape of one QSA layer. */
+typedef struct {
+  int32_t num_q_heads;       /* H_q; a multiple of num_kv_heads                    */
+  int32_t num_kv_heads;      /* H_kv; query head h reads KV head h / (H_q/H_kv)    */
+  int32_t head_dim;          /* d: 64 or 128                                       */
+  int32_t index_dim;         /* D: 32, 64 or 128                                   */
+  int32_t compress_ratio;    /* tokens per micro-block; must be 4 ([QSA-DCP])      */
+  int32_t topk_blocks;       /* k: 1..2048 (512 in [QSA-DCP])                      */
+  int32_t page_size;         /* tokens per page: power of two, >= 16 ([PR53896]:
+                                the ratio must divide the block size)             */
+  int32_t max_pages_per_req; /* row stride of block_table                         */
+  int32_t kv_dtype;          /* qsa_kv_dtype                                       */
+  float softmax_scale;       /* logits are scale * q.k (1/sqrt(d) usually)         */
+} qsa_config;
+
+/* Largest context one row may have: 2^21 micro-blocks (8,388,608 tokens). */
+#define QSA_MAX_SEQ_LEN (4 * (1 << 21))
+
+/* Bytes of the compressed-key cache for `num_pages` pages; 0 on a bad config. */
+size_t qsa_ckey_cache_bytes(const qsa_config* cfg, int64_t num_pages);
+
+/*
+ * qsa_compress -- append new tokens' indexer keys; close micro-blocks.
+ *   [QSA-DCP] keys are compressed into micro-blocks of 4 tokens; [PR53896] the
+ *   raw keys go through a ring and are pooled into the compressed key cache.
+ *
+ * Request b (0 <= b < num_reqs) appends rows [new_cu[b], new_cu[b+1]) of
+ * new_keys (int8 [T_new, D]) as tokens seq_len_before[b], seq_len_before[b]+1, ...
+ * Every micro-block j whose last token 4j+3 is among them gets
+ * C_j = k_{4j} + k_{4j+1} + k_{4j+2} + k_{4j+3} written to ckey_cache; keys of
+ * tokens before seq_len_before[b] that C_j needs come from ring[b]; the new
+ * tokens of the block left open are written to ring[b].  Any number of new
+ * tokens and any seq_len_before are handled (bulk prefill and decode alike).
+ * Requests with seq_len_before[b] < 0 or no new tokens write nothing
+ * ([QSA-DCP]: dummy batches must not write the side cache).
+ *   max_new_tokens: host-side upper bound of new_cu[b+1]-new_cu[b] (sizes the grid;
+ *                   a larger count is still handled correctly, just slower).
+ * Errors: INVALID_ARGUMENT (null pointer, num_reqs < 0, bad config),
+ *         UNSUPPORTED (index_dim), HIP.
+ */
+qsa_status qsa_compress(const qsa_config* cfg, int32_t num_reqs, int32_t max_new_tokens,
+                        const int8_t* new_keys, const int32_t* new_cu,
+                        const int32_t* seq_len_before, const int32_t* block_table,
+                        int8_t* ring, int8_t* ckey_cache, hipStream_t stream);
+
+/*
+ * Workspace of qsa_index_topk for num_sel_rows rows of context <= max_seq_len.
+ * Returns 0 on a bad argument.  Before its FIRST use a workspace must be
+ * cleared with qsa_index_topk_workspace_init(); every qsa_index_topk call
+ * leaves its counters cleared again, so later calls need no clearing.
+ */
+size_t qsa_index_topk_workspace_size(const qsa_config* cfg, int32_t num_sel_rows,
+                                     int32_t max_seq_len);
+qsa_status qsa_index_topk_workspace_init(void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * qsa_index_topk -- score every closed micro-block against the indexer query
+ * and keep the best k.  [QSA-DCP]: keep the best 512 blocks; [PR53896]:
+ * weight-free top-k over the compressed keys, fixed-width int32 output padded
+ * with -1.
+ *
+ * Selecting row s (0 <= s < num_sel_rows) belongs to request sel_req[s] and has
+ * context L = sel_seq_len[s] (all cached tokens, its own included).  Blocks
+ * j < floor(L/4) are scored exactly: score_j = sum_i q_index[s][i] * C_j[i]
+ * (int32, no overflow for D <= 128).  The best min(k, floor(L/4)) blocks by
+ * (score descending, block index ascending) are written to topk[s] (int32 [S, k])
+ * in ascending block order, followed by -1.  Rows with L < 4 get all -1.
+ * Ties are broken towards the lower block index, so the result is unique.
+ *   max_seq_len: host-side bound of sel_seq_len (<= QSA_MAX_SEQ_LEN); it sizes
+ *                the grid and the workspace.  Rows longer than it are treated
+ *                as max_seq_len long.
+ *   topk == NULL: score only.  The exact int32 scores are left in the first
+ *                num_sel_rows * nb_stride * 4 bytes of the workspace (row s,
+ *                block j at [s * nb_stride + j], nb_stride = max_seq_len/4
+ *                rounded up to a multiple of 1024) and nothing is selected.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (index_dim), WORKSPACE, HIP.
+ */
+qsa_status qsa_index_topk(const qsa_config* cfg, int32_t num_sel_rows, int32_t max_seq_len,
+                          const int8_t* q_index, const int32_t* sel_req,
+                          const int32_t* sel_seq_len, const int32_t* block_table,
+                          const int8_t* ckey_cache, int32_t* topk,
+                          void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * qsa_sparse_decode -- attention of the query rows over the selected tokens,
+ * as num_splits partial results.  [QSA-DCP]: softmax and value aggregation over
+ * the uncompressed K/V at the kept positions; each context-parallel partition
+ * yields a partial result that is merged at the end (qsa_merge_partials).
+ *
+ * Rows r = s*q_per_sel + i (i < q_per_sel) share selecting row s: same request
+ * sel_req[s], same topk[s] ([PR53896]: a later MTP step reuses the selection).
+ * Row r attends tokens {4j..4j+3 : j in topk[s], j >= 0} plus its own tail
+ * [4*floor(sel_seq_len[s]/4), row_seq_len[r]) (the open block it could not
+ * score).  row_seq_len[r] >= sel_seq_len[s] is required.
+ * Split p of P owns selected blocks [floor(p*n/P), floor((p+1)*n/P)) of the n
+ * valid ones, and split P-1 also owns the tail.  For query head h (KV head
+ * h / (H_q/H_kv)):
+ *   z_t = softmax_scale * q[r][h] . K_t   (fp8: times k_scale of token t)
+ *   lse_part[p][r][h] = log sum_t exp(z_t)                 (natural log)
+ *   o_part[p][r][h][:] = sum_t exp(z_t - lse) V_t          (fp8: V_t * v_scale_t)
+ * An empty split gives o_part = 0, lse_part = -inf.
+ *   q        bf16 [S*q_per_sel, H_q, d]
+ *   o_part   fp32 [P, S*q_per_sel, H_q, d];  lse_part fp32 [P, S*q_per_sel, H_q]
+ *   num_splits in [1, 64]; q_per_sel * (H_q/H_kv) <= 64.
+ *   k_scale / v_scale are required for fp8 and ignored for bf16.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (head_dim, group size), HIP.
+ */
+qsa_status qsa_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_t q_per_sel,
+                             int32_t num_splits, const void* q, const int32_t* row_seq_len,
+                             const int32_t* sel_req, const int32_t* sel_seq_len,
+                             const int32_t* topk, const int32_t* block_table,
+                             const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale,
+                             float* o_part, float* lse_part, hipStream_t stream);
+
+/*
+ * qsa_merge_partials -- log-sum-exp merge of the split partials ([QSA-DCP]:
+ * partial attention results of the context partitions are merged at the end).
+ *   lse[r][h] = M + log sum_p exp(lse_part[p][r][h] - M),  M = max_p lse_part
+ *   out[r][h] = sum_p exp(lse_part[p][r][h] - lse[r][h]) * o_part[p][r][h]
+ * If every split is empty (all -inf): out = 0, lse = -inf.
+ *   o_part fp32 [P, R, H, d], lse_part fp32 [P, R, H], lse fp32 [R, H];
+ *   out [R, H, d] is fp32 (out_dtype QSA_OUT_F32) or bf16 rounded to nearest
+ *   even from the same fp32 value (QSA_OUT_BF16).
+ *   num_splits in [1, 64]; head_dim 64 or 128.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (head_dim), HIP.
+ */
+typedef enum { QSA_OUT_F32 = 0, QSA_OUT_BF16 = 1 } qsa_out_dtype;
+
+qsa_status qsa_merge_partials(int32_t num_splits, int32_t num_rows, int32_t num_heads,
+                              int32_t head_dim, const float* o_part, const float* lse_part,
+                              void* out, int32_t out_dtype, float* lse, hipStream_t stream);
+
+/* Human-readable name of a status. */
+const char* qsa_status_string(qsa_status status);
+
+/* Description of the last failed call on this thread ("" if none). */
+const char* qsa_last_error(void);
+
+/* Library version, e.g. "qsa-mi355x 0.1.0". */
+const char* qsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H_ */

@@ -26,3 +26,12 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _libqsa_built():
+    """Build libqsa.so in-tree if it is not there yet (hipcc cross-compiles for gfx950)."""
+    from block_sparse_attention_qsa_amd import _lib, build
+    if not os.path.exists(_lib.LIB_PATH):
+        build.build()
+    yield

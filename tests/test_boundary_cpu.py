@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and rejects bad arguments on the host before enqueueing anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_sparse_attention_qsa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def cfg(**kw):
+    base = dict(num_q_heads=16, num_kv_heads=2, head_dim=128, index_dim=64, compress_ratio=4,
+                topk_blocks=512, page_size=64, max_pages_per_req=4096, kv_dtype=0, softmax_scale=0.088)
+    base.update(kw)
+    return _lib.qsa_config(**base)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"qsa_compress", "qsa_index_topk", "qsa_sparse_decode", "qsa_merge_partials"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\b(qsa_[a-z0-9_]+)\b", out))
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.qsa_version().startswith(b"qsa-mi355x")
+    assert lib.qsa_status_string(0) == b"QSA_OK"
+    assert lib.qsa_status_string(3) == b"QSA_ERR_WORKSPACE"
+    assert lib.qsa_status_string(99) == b"QSA_ERR_UNKNOWN"
+
+
+def compress(lib, c, nreq=1, **kw):
+    a = dict(new_keys=FAKE, new_cu=FAKE, before=FAKE, bt=FAKE, ring=FAKE, ckey=FAKE)
+    a.update(kw)
+    return lib.qsa_compress(ctypes.byref(c), nreq, 4, a["new_keys"], a["new_cu"], a["before"], a["bt"],
+                            a["ring"], a["ckey"], None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(compress_ratio=3), 1), (dict(compress_ratio=8), 1), (dict(page_size=48), 1),
+    (dict(page_size=8), 1), (dict(topk_blocks=0), 1), (dict(topk_blocks=4096), 1),
+    (dict(max_pages_per_req=0), 1), (dict(index_dim=48), 2), (dict(index_dim=0), 1),
+])
+def test_compress_rejects_bad_config(lib, bad, code):
+    assert compress(lib, cfg(**bad)) == code
+    assert lib.qsa_last_error() != b""
+
+
+def test_compress_rejects_null_and_misaligned(lib):
+    assert compress(lib, cfg(), ckey=None) == 1
+    assert compress(lib, cfg(), ring=None) == 1
+    assert compress(lib, cfg(), ckey=ctypes.c_void_p(0x10004)) == 1
+    assert compress(lib, cfg(), nreq=-1) == 1
+    assert compress(lib, cfg(), nreq=0) == 0  # nothing to do, nothing enqueued
+    assert lib.qsa_ckey_cache_bytes(ctypes.byref(cfg()), 10) == 10 * 64 // 4 * 2 * 64
+    assert lib.qsa_ckey_cache_bytes(ctypes.byref(cfg(compress_ratio=2)), 10) == 0
+
+
+def test_workspace_size_and_checks(lib):
+    c = cfg()
+    n8 = lib.qsa_index_topk_workspace_size(ctypes.byref(c), 8, 262144)
+    n16 = lib.qsa_index_topk_workspace_size(ctypes.byref(c), 16, 262144)
+    assert 0 < n8 < n16
+    assert lib.qsa_index_topk_workspace_size(ctypes.byref(c), 8, _lib.QSA_MAX_SEQ_LEN + 1) == 0
+    assert lib.qsa_index_topk_workspace_size(ctypes.byref(c), -1, 100) == 0
+
+    def topk(ws=FAKE, nbytes=n8, S=8, L=262144, **kw):
+        return lib.qsa_index_topk(ctypes.byref(kw.get("c", c)), S, L, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  ws, nbytes, None)
+    assert topk(nbytes=n8 - 1) == 3
+    assert topk(ws=None) == 3
+    assert topk(ws=ctypes.c_void_p(0x10010)) == 3  # not 256-aligned
+    assert topk(L=_lib.QSA_MAX_SEQ_LEN + 4) == 1
+    assert topk(S=-2) == 1
+    assert topk(c=cfg(index_dim=96)) == 2
+    assert topk(S=0) == 0
+    assert lib.qsa_index_topk_workspace_init(None, 100, None) == 3
+
+
+def decode(lib, c, P=2, qps=1, S=4, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, o=FAKE, l=FAKE)
+    a.update(kw)
+    return lib.qsa_sparse_decode(ctypes.byref(c), S, qps, P, a["q"], FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 a["k"], a["v"], a["ks"], a["vs"], a["o"], a["l"], None)
+
+
+def test_decode_rejects(lib):
+    assert decode(lib, cfg(num_q_heads=15)) == 1
+    assert decode(lib, cfg(head_dim=96)) == 2
+    assert decode(lib, cfg(kv_dtype=7)) == 2
+    assert decode(lib, cfg(softmax_scale=0.0)) == 1
+    assert decode(lib, cfg(), P=0) == 1
+    assert decode(lib, cfg(), P=65) == 1
+    assert decode(lib, cfg(), qps=0) == 1
+    assert decode(lib, cfg(), qps=9) == 2          # 8 heads x 9 rows > 64
+    assert decode(lib, cfg(kv_dtype=1)) == 1       # fp8 without scales
+    assert decode(lib, cfg(), q=None) == 1
+    assert decode(lib, cfg(), k=ctypes.c_void_p(0x10008)) == 1
+    assert decode(lib, cfg(), S=0) == 0
+
+
+def test_merge_rejects(lib):
+    assert lib.qsa_merge_partials(0, 4, 16, 128, FAKE, FAKE, FAKE, 0, FAKE, None) == 1
+    assert lib.qsa_merge_partials(65, 4, 16, 128, FAKE, FAKE, FAKE, 0, FAKE, None) == 1
+    assert lib.qsa_merge_partials(2, 4, 16, 96, FAKE, FAKE, FAKE, 0, FAKE, None) == 2
+    assert lib.qsa_merge_partials(2, 4, 16, 128, None, FAKE, FAKE, 0, FAKE, None) == 1
+    assert lib.qsa_merge_partials(2, 4, 16, 128, FAKE, FAKE, FAKE, 2, FAKE, None) == 1
+    assert lib.qsa_merge_partials(2, 0, 16, 128, None, None, None, 1, None, None) == 0
+
+
+def test_python_binding_raises_with_message():
+    from block_sparse_attention_qsa_amd import api
+    bad = api.QSAConfig(16, 2, 128, 64, 512, 48, 10)
+    with pytest.raises(api.QSAError, match="page_size"):
+        api._check(_lib.load().qsa_compress(ctypes.byref(bad.to_c()), 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            FAKE, None))
