@@ -72,6 +72,21 @@ struct DecodeArgs {
   float scale_log2;  // softmax_scale * log2(e)
 };
 
+// Token-slot view of one split: slot u covers token 4*blk(u/4) + u%4, where
+// blk(i) is the i-th selected block of the split, or a block of the tail.
+constexpr int kRound = 512;  // blocks staged in LDS per round
+
+template <int D, bool FP8>
+struct TileLoad {
+  static constexpr int KK = D / 32;
+  static constexpr int DPL = D / 64;
+  i32x4 k[FP8 ? 1 : KK];   // bf16: 16 B per k-step
+  i32x2 k8[FP8 ? KK : 1];  // fp8: 8 B per k-step
+  uint32_t v[16];          // this lane's V bytes of each of the 16 slots
+  int t;                   // token of slot lc (-1: none)
+  float ks, vs;            // fp8 scales of slot lc
+};
+
 template <int D, int NH, bool FP8>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   constexpr int NT = (NH + 15) / 16;  // MFMA N tiles of 16 heads
@@ -83,6 +98,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   __shared__ float alpha_lds[kWaves][NH];
   __shared__ float ml_lds[kWaves][2][NH];
   __shared__ float o_sh[NH][D];
+  __shared__ int32_t blk_tok[kRound];   // first token of each staged block
+  __shared__ int32_t blk_pos[kRound];   // its position in the page pool (page*page_size + slot)
 
   const int p = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
   const int l = lane_id(), w = threadIdx.x / 64;
@@ -97,9 +114,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int tail_lo = 4 * (Lsel >> 2);
   int tail_hi = 0;
   for (int i = 0; i < a.qps; ++i) tail_hi = max(tail_hi, a.row_seq_len[s * a.qps + i]);
-  const int ntail = (p == a.P - 1) ? max(0, tail_hi - tail_lo) : 0;
-  const int nslots = 4 * nblk + ntail;
-  const int ntiles = (nslots + 15) >> 4;
+  const int ntailblk = (p == a.P - 1) ? (max(0, tail_hi - tail_lo) + 3) >> 2 : 0;
+  const int nall = nblk + ntailblk;  // blocks of this split (selected, then tail)
   const int page_size = 1 << a.page_log2;
   const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
   const int32_t* sel = a.topk + (size_t)s * a.k + lo;
@@ -134,133 +150,151 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const char* kbase = reinterpret_cast<const char*>(a.k_cache);
   const char* vbase = reinterpret_cast<const char*>(a.v_cache);
 
-  for (int ti = w; ti < ntiles; ti += kWaves) {
-    // ---- token of slot u = 16*ti + lc (every lane group holds the same 16) ----
-    const int u = ti * 16 + lc;
-    int t = -1;
-    if (u < 4 * nblk) {
-      const int j = sel[u >> 2];
-      t = (j >= 0) ? 4 * j + (u & 3) : -1;
-    } else if (u < nslots) {
-      t = tail_lo + (u - 4 * nblk);
-    }
-    // Invalid slots (past the end of the split) read row 0 of the cache, a
-    // valid address, and are masked below: loads stay unconditional.
-    int row = -1;  // token row index inside the cache for this KV head
-    int pg = 0, sl = 0;
-    if (t >= 0) {
-      pg = bt[t >> a.page_log2];
-      sl = t & (page_size - 1);
-      row = (pg * a.Hkv + kvh) * page_size + sl;
-    }
-    const int rowc = max(row, 0);
-    float ks = 1.f, vs = 1.f;
-    if (FP8) {
-      ks = a.k_scale[(size_t)pg * page_size + sl];
-      vs = a.v_scale[(size_t)pg * page_size + sl];
-    }
-    // ---- loads: K tile into A operands, V rows (one per slot) ----
-    bf16x8 ak[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (FP8) {
-        i32x2 v = *reinterpret_cast<const i32x2*>(kbase + (size_t)rowc * D + 32 * kk + 8 * lg);
-        ak[kk] = fp8x8_to_bf16x8(v);
+  for (int r0 = 0; r0 < nall; r0 += kRound) {
+    const int nr = min(kRound, nall - r0);
+    // ---- stage block ids and page positions of this round in LDS ----
+    __syncthreads();
+    for (int i = threadIdx.x; i < nr; i += kThreads) {
+      const int u = r0 + i;
+      int tok = -1, pos = 0;
+      if (u < nblk) {
+        const int j = sel[u];
+        tok = (j >= 0) ? 4 * j : -1;
       } else {
-        i32x4 v = ld16(kbase + ((size_t)rowc * D + 32 * kk + 8 * lg) * 2);
-        ak[kk] = __builtin_bit_cast(bf16x8, v);
+        tok = tail_lo + 4 * (u - nblk);
       }
+      if (tok >= 0) pos = (bt[tok >> a.page_log2] << a.page_log2) | (tok & (page_size - 1));
+      blk_tok[i] = tok;
+      blk_pos[i] = pos;
     }
-    uint32_t vv[16];
+    __syncthreads();
+    const int ntiles = (nr + 3) >> 2;
+
+    // Slot lc of tile ti: block 4*ti + lc/4 of the round, token offset lc%4.
+    auto issue = [&](int ti, TileLoad<D, FP8>& tl) {
+      const int bi = 4 * ti + (lc >> 2);
+      int t = -1, pos = 0;
+      if (bi < nr) {
+        const int tok = blk_tok[bi];
+        if (tok >= 0) { t = tok + (lc & 3); pos = blk_pos[bi] + (lc & 3); }
+      }
+      // slots without a token read row 0 of the cache (a valid address) and are masked
+      const int row = (t >= 0) ? ((((pos >> a.page_log2) * a.Hkv + kvh) << a.page_log2) | (pos & (page_size - 1))) : 0;
+      tl.t = t;
+      if (FP8) {
+        tl.ks = a.k_scale[pos];
+        tl.vs = a.v_scale[pos];
 #pragma unroll
-    for (int uu = 0; uu < 16; ++uu) {
-      const int r = __builtin_amdgcn_readlane(rowc, uu);
-      const char* vp = vbase + ((size_t)r * D + (size_t)l * DPL) * ES;
-      if (ES * DPL == 4) vv[uu] = *reinterpret_cast<const uint32_t*>(vp);
-      else if (ES * DPL == 2) vv[uu] = *reinterpret_cast<const uint16_t*>(vp);
-      else vv[uu] = *reinterpret_cast<const uint8_t*>(vp);
-    }
-    // ---- S^T = K Q^T ----
-    f32x4 c[NT];
+        for (int kk = 0; kk < KK; ++kk)
+          tl.k8[kk] = *reinterpret_cast<const i32x2*>(kbase + (size_t)row * D + 32 * kk + 8 * lg);
+      } else {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      c[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < KK; ++kk) tl.k[kk] = ld16(kbase + ((size_t)row * D + 32 * kk + 8 * lg) * 2);
+      }
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        c[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[kk], bq[nt][kk], c[nt], 0, 0, 0);
-    }
-    // C layout: lane (lc, lg) holds slots 4*lg+e (e<4) for head nt*16+lc.
-    int tc[4];
-    float ksc[4], vsc[4];
+      for (int uu = 0; uu < 16; ++uu) {
+        const int r = __builtin_amdgcn_readlane(row, uu);
+        const char* vp = vbase + ((size_t)r * D + (size_t)l * DPL) * ES;
+        if (ES * DPL == 4) tl.v[uu] = *reinterpret_cast<const uint32_t*>(vp);
+        else if (ES * DPL == 2) tl.v[uu] = *reinterpret_cast<const uint16_t*>(vp);
+        else tl.v[uu] = *reinterpret_cast<const uint8_t*>(vp);
+      }
+    };
+
+    TileLoad<D, FP8> cur, nxt;
+    int ti = w;
+    if (ti < ntiles) issue(ti, cur);
+    for (; ti < ntiles; ti += kWaves) {
+      if (ti + kWaves < ntiles) issue(ti + kWaves, nxt);
+      // ---- S^T = K Q^T ----
+      bf16x8 ak[KK];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tc[e] = __shfl(t, 4 * lg + e, 64);
-      if (FP8) { ksc[e] = __shfl(ks, 4 * lg + e, 64); vsc[e] = __shfl(vs, 4 * lg + e, 64); }
-    }
+      for (int kk = 0; kk < KK; ++kk) {
+        if (FP8) ak[kk] = fp8x8_to_bf16x8(cur.k8[kk]);
+        else ak[kk] = __builtin_bit_cast(bf16x8, cur.k[kk]);
+      }
+      f32x4 c[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float z[4];
-      float mt = -INFINITY;
+      for (int nt = 0; nt < NT; ++nt) {
+        c[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          c[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[kk], bq[nt][kk], c[nt], 0, 0, 0);
+      }
+      // C layout: lane (lc, lg) holds slots 4*lg+e (e<4) for head nt*16+lc.
+      int tc[4];
+      float ksc[4], vsc[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const bool ok = tc[e] >= 0 && tc[e] < rlen[nt];
-        float zz = c[nt][e] * a.scale_log2;
-        if (FP8) zz *= ksc[e];
-        z[e] = ok ? zz : -INFINITY;
-        mt = fmaxf(mt, z[e]);
+        tc[e] = __shfl(cur.t, 4 * lg + e, 64);
+        if (FP8) { ksc[e] = __shfl(cur.ks, 4 * lg + e, 64); vsc[e] = __shfl(cur.vs, 4 * lg + e, 64); }
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run[nt], mt);
-      float alpha, ps = 0.f;
-      float pe[4];
-      if (m_new == -INFINITY) {
-        alpha = 1.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pe[e] = 0.f;
-      } else {
-        alpha = exp2f(m_run[nt] - m_new);
+      for (int nt = 0; nt < NT; ++nt) {
+        float z[4];
+        float mt = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { pe[e] = exp2f(z[e] - m_new); ps += pe[e]; }
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = tc[e] >= 0 && tc[e] < rlen[nt];
+          float zz = c[nt][e] * a.scale_log2;
+          if (FP8) zz *= ksc[e];
+          z[e] = ok ? zz : -INFINITY;
+          mt = fmaxf(mt, z[e]);
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float m_new = fmaxf(m_run[nt], mt);
+        float alpha, ps = 0.f;
+        float pe[4];
+        if (m_new == -INFINITY) {
+          alpha = 1.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pe[e] = 0.f;
+        } else {
+          alpha = exp2f(m_run[nt] - m_new);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { pe[e] = exp2f(z[e] - m_new); ps += pe[e]; }
+        }
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        l_run[nt] = l_run[nt] * alpha + ps;
+        m_run[nt] = m_new;
+        const int n = nt * 16 + lc;
+        if (n < NH) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p_lds[w][4 * lg + e][n] = FP8 ? pe[e] * vsc[e] : pe[e];
+          if (lg == 0) alpha_lds[w][n] = alpha;
+        }
       }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
-      l_run[nt] = l_run[nt] * alpha + ps;
-      m_run[nt] = m_new;
-      const int n = nt * 16 + lc;
-      if (n < NH) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p_lds[w][4 * lg + e][n] = FP8 ? pe[e] * vsc[e] : pe[e];
-        if (lg == 0) alpha_lds[w][n] = alpha;
-      }
-    }
-    wave_sync_lds();
-    // ---- O = alpha O + P V ----
-#pragma unroll
-    for (int n = 0; n < NH; ++n) {
-      const float al = alpha_lds[w][n];
-#pragma unroll
-      for (int j = 0; j < DPL; ++j) o[n][j] *= al;
-    }
-#pragma unroll
-    for (int uu = 0; uu < 16; ++uu) {
-      float vf[DPL];
-      if (FP8) {
-        auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)vv[uu], false);
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) vf[j] = f[j];
-      } else {
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) vf[j] = bf16_bits_to_f32((vv[uu] >> (16 * j)) & 0xffffu);
-      }
+      wave_sync_lds();
+      // ---- O = alpha O + P V ----
 #pragma unroll
       for (int n = 0; n < NH; ++n) {
-        const float pn = p_lds[w][uu][n];
+        const float al = alpha_lds[w][n];
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) o[n][j] = fmaf(pn, vf[j], o[n][j]);
+        for (int j = 0; j < DPL; ++j) o[n][j] *= al;
       }
+#pragma unroll
+      for (int uu = 0; uu < 16; ++uu) {
+        float vf[DPL];
+        if (FP8) {
+          auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)cur.v[uu], false);
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) vf[j] = f[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) vf[j] = bf16_bits_to_f32((cur.v[uu] >> (16 * j)) & 0xffffu);
+        }
+#pragma unroll
+        for (int n = 0; n < NH; ++n) {
+          const float pn = p_lds[w][uu][n];
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) o[n][j] = fmaf(pn, vf[j], o[n][j]);
+        }
+      }
+      wave_sync_lds();
+      cur = nxt;
     }
-    wave_sync_lds();
   }
 
   // ---- merge the four waves (fixed order => deterministic) ----
@@ -332,13 +366,13 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
     const float sum = wave_sum(wgt);
     if (l == 0) lse[rh] = M + logf(sum);
     const float inv = 1.f / sum;
+#pragma unroll 8
     for (int pp = 0; pp < P; ++pp) {
+      // empty partials have weight 0 and finite (zero) outputs: no branch
       const float wp = __shfl(wgt, pp, 64) * inv;
-      if (wp != 0.f) {
-        const float* src = o_part + ((size_t)pp * RH + rh) * D + l * DPL;
+      const float* src = o_part + ((size_t)pp * RH + rh) * D + l * DPL;
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) acc[j] = fmaf(wp, src[j], acc[j]);
-      }
+      for (int j = 0; j < DPL; ++j) acc[j] = fmaf(wp, src[j], acc[j]);
     }
   }
 #pragma unroll

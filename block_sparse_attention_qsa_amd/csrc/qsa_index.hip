@@ -7,21 +7,22 @@
 // int32 buffer padded with -1.  Ties go to the lower block index, so the
 // result is unique and can be compared bit for bit.
 //
-// Two kernels, both gridded (chunk of 1024 micro-blocks, selecting row):
-//   score:  streams the 2-byte compressed keys (the HBM-bound scan), computes
-//           score = q.lo + 256 q.hi with v_dot4_i32_i8, stores the int32 score,
-//           and adds an LDS histogram of the score's top 11 bits to a per-row
-//           global histogram.  The last workgroup of a row finds the threshold
-//           bin T: fewer than k scores lie in bins above T, at least k in bins
-//           >= T.
-//   select: re-reads the scores (L2 / MALL resident), writes a bitmap of the
-//           blocks strictly above T and appends 64-bit keys (score, ~index) of
-//           the blocks inside T to a candidate list.  The last workgroup of a
-//           row radix-selects the missing blocks among the candidates (usually
-//           a few hundred), sets their bits, and emits the bitmap in ascending
-//           order with a popcount prefix sum, padding with -1.
-// Counters and the histogram are cleared by the workgroup that consumed them,
-// so the workspace stays clean between calls.
+// Three kernels, no fences and no inter-workgroup waits (each kernel boundary
+// publishes the previous kernel's results):
+//   score    (grid: chunk of 1024 micro-blocks x selecting row): streams the
+//            2-byte compressed keys (the HBM-bound scan), computes
+//            score = q.lo + 256 q.hi with v_dot4_i32_i8, stores the int32 score
+//            and adds an LDS histogram of the score's top 11 bits into a
+//            per-row histogram with device-scope atomics.
+//   filter   (same grid): each workgroup derives the threshold bin T from the
+//            row histogram (fewer than k scores above T, at least k at or above
+//            it), writes bitmap words of its blocks above T and appends 64-bit
+//            keys (score, ~index) of its blocks inside T to the row's list.
+//   finalize (one workgroup per selecting row): radix-selects the missing
+//            blocks among the candidates (usually a few hundred), sets their
+//            bits, emits the bitmap in ascending order with a popcount prefix
+//            sum and pads with -1.  It clears the row's histogram and candidate
+//            count, so the workspace stays clean between calls.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -30,16 +31,15 @@ namespace qsa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 constexpr int kIters = kScoreChunk / kThreads;
 
 struct WsPtrs {
   int32_t* scores;
   uint64_t* keys;
   uint64_t* bitmap;
+  uint64_t* keys2;
   uint32_t* hist;
-  uint32_t* ctr;
-  int32_t* meta;
+  uint32_t* ccount;
   int32_t nb_stride;
 };
 
@@ -51,34 +51,13 @@ __device__ __forceinline__ uint64_t cand_key(int32_t score, uint32_t j) {
   return ((uint64_t)((uint32_t)score ^ 0x80000000u) << 32) | (uint64_t)(0xffffffffu - j);
 }
 
-// Block-wide exclusive prefix sum of one value per thread (256 threads).
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh /*[kWaves+1]*/,
-                                                    uint32_t* total) {
-  const int l = lane_id(), w = threadIdx.x / 64;
-  uint32_t inc = wave_incl_scan(v);
-  if (l == 63) sh[w] = inc;
-  __syncthreads();
-  uint32_t off = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    const uint32_t x = sh[i];
-    off += (i < w) ? x : 0u;
-    tot += x;
-  }
-  __syncthreads();
-  *total = tot;
-  return off + inc - v;
-}
-
 template <int D>
 __global__ __launch_bounds__(kThreads) void score_kernel(
     const int8_t* __restrict__ q_index, const int32_t* __restrict__ sel_req,
     const int32_t* __restrict__ sel_seq_len, const int32_t* __restrict__ block_table,
-    int32_t max_pages, int32_t page_log2, const int8_t* __restrict__ ckey, int32_t k,
+    int32_t max_pages, int32_t page_log2, const int8_t* __restrict__ ckey,
     int32_t max_seq_len, WsPtrs ws) {
   __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t sh[kWaves + 1];
-  __shared__ int is_last;
   const int s = blockIdx.y;
   const int c = blockIdx.x;
   const int L = min(sel_seq_len[s], max_seq_len);
@@ -90,114 +69,132 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
   const int bpp = 1 << bpp_log2;
   const size_t page_bytes = (size_t)bpp * 2 * D;
 
+  for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0;
+
+  // Page ids of this thread's kIters blocks first (one round trip), then all
+  // compressed-key loads at once, then the arithmetic.
+  const int32_t* bt = block_table + (size_t)b * max_pages;
+  int page[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int j = c * kScoreChunk + it * kThreads + threadIdx.x;
+    page[it] = (j < nb) ? bt[j >> bpp_log2] : 0;
+  }
   // indexer query: D int8 = D/4 packed dwords, uniform across the workgroup
   int32_t qw[D / 4];
   const int32_t* q32 = reinterpret_cast<const int32_t*>(q_index + (size_t)s * D);
 #pragma unroll
   for (int i = 0; i < D / 4; ++i) qw[i] = q32[i];
 
-  for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0;
-  __syncthreads();
-
-  const int32_t* bt = block_table + (size_t)b * max_pages;
-  int32_t* srow = ws.scores + (size_t)s * ws.nb_stride;
-#pragma unroll 2
+  i32x4 v[kIters][D / 8];
+#pragma unroll
   for (int it = 0; it < kIters; ++it) {
     const int j = c * kScoreChunk + it * kThreads + threadIdx.x;
-    if (j < nb) {
-      const int page = bt[j >> bpp_log2];
-      const int8_t* base = ckey + (size_t)page * page_bytes + (size_t)(j & (bpp - 1)) * 16;
-      i32x4 v[D / 8];
+    const int8_t* base = ckey + (size_t)page[it] * page_bytes + (size_t)(j & (bpp - 1)) * 16;
 #pragma unroll
-      for (int ch = 0; ch < D / 8; ++ch) v[ch] = ld16(base + (size_t)ch * bpp * 16);
-      int32_t lo = 0, hi = 0;
+    for (int ch = 0; ch < D / 8; ++ch)
+      v[it][ch] = (j < nb) ? ld16(base + (size_t)ch * bpp * 16) : i32x4{0, 0, 0, 0};
+  }
+  __syncthreads();  // hist cleared
+  int32_t* srow = ws.scores + (size_t)s * ws.nb_stride;
 #pragma unroll
-      for (int ch = 0; ch < D / 16; ++ch) {
+  for (int it = 0; it < kIters; ++it) {
+    const int j = c * kScoreChunk + it * kThreads + threadIdx.x;
+    int32_t lo = 0, hi = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lo = __builtin_amdgcn_sdot4(v[ch][e], qw[4 * ch + e], lo, false);
-          hi = __builtin_amdgcn_sdot4(v[ch + D / 16][e], qw[4 * ch + e], hi, false);
-        }
+    for (int ch = 0; ch < D / 16; ++ch) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo = __builtin_amdgcn_sdot4(v[it][ch][e], qw[4 * ch + e], lo, false);
+        hi = __builtin_amdgcn_sdot4(v[it][ch + D / 16][e], qw[4 * ch + e], hi, false);
       }
-      const int32_t score = lo + hi * 256;
+    }
+    const int32_t score = lo + hi * 256;
+    if (j < nb) {
       srow[j] = score;
       atomicAdd(&hist[score_bin(score)], 1u);
     }
   }
   __syncthreads();
+  // Per-row histogram in the workspace: device-scope atomics, read by the
+  // next kernel after this one has finished (no fence needed here).
   uint32_t* ghist = ws.hist + (size_t)s * kBins;
   for (int i = threadIdx.x; i < kBins; i += kThreads) {
     const uint32_t h = hist[i];
     if (h) atomicAdd(&ghist[i], h);
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = (atomicAdd(&ws.ctr[4 * s + 0], 1u) == (uint32_t)(nchunks - 1));
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-
-  // Last workgroup of the row: threshold bin from the top.
-  const uint32_t ks = (uint32_t)min(k, nb);
-  constexpr int kPer = kBins / kThreads;  // 8 bins per thread, thread t owns the
-  // bins [kBins-1-kPer*t-(kPer-1), kBins-1-kPer*t] (descending from the top)
-  uint32_t cnt[kPer];
-  uint32_t mine = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int bin = kBins - 1 - (kPer * threadIdx.x + i);
-    cnt[i] = ld_acq_u32(&ghist[bin]);
-    mine += cnt[i];
-  }
-  uint32_t total;
-  uint32_t above = block_excl_scan(mine, sh, &total);  // count in higher bins
-  // The thread whose bins contain the k-th largest records the threshold.
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int bin = kBins - 1 - (kPer * threadIdx.x + i);
-    if (above < ks && above + cnt[i] >= ks) {
-      ws.meta[2 * s + 0] = bin;
-      ws.meta[2 * s + 1] = (int32_t)above;
-    }
-    above += cnt[i];
-  }
-  // clear for the next call
-  for (int i = threadIdx.x; i < kBins; i += kThreads) ghist[i] = 0;
-  if (threadIdx.x == 0) ws.ctr[4 * s + 0] = 0;
 }
 
-__global__ __launch_bounds__(kThreads) void select_kernel(
-    const int32_t* __restrict__ sel_seq_len, int32_t k, int32_t max_seq_len,
-    int32_t* __restrict__ topk, WsPtrs ws) {
-  __shared__ uint32_t sh[kWaves + 1];
-  __shared__ uint32_t rhist[256];
-  __shared__ int is_last;
-  __shared__ uint32_t s_info[4];
+// Block-wide exclusive prefix sum (blockDim.x threads, a multiple of 64).
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh /*[NT/64]*/) {
+  const int l = lane_id(), w = threadIdx.x / 64;
+  const uint32_t inc = wave_incl_scan(v);
+  if (l == 63) sh[w] = inc;
+  __syncthreads();
+  uint32_t off = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) off += (i < w) ? sh[i] : 0u;
+  __syncthreads();
+  return off + inc - v;
+}
+
+// Threshold bin from the row histogram: the bin T with
+// count(bins > T) < ks <= count(bins >= T).  Returns (T, count above T).
+template <int NT>
+__device__ __forceinline__ void find_threshold(const uint32_t* ghist, uint32_t ks, uint32_t* sh,
+                                               int32_t* s_T, uint32_t* s_above) {
+  constexpr int kPer = kBins / NT;
+  const int tid = threadIdx.x;
+  uint32_t cnt[kPer], mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    cnt[i] = ghist[kBins - 1 - (kPer * tid + i)];
+    mine += cnt[i];
+  }
+  uint32_t above = block_excl_scan<NT>(mine, sh);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (above < ks && above + cnt[i] >= ks) { *s_T = kBins - 1 - (kPer * tid + i); *s_above = above; }
+    above += cnt[i];
+  }
+  __syncthreads();
+}
+
+// Filter (grid: chunk x selecting row): blocks in bins above T -> bitmap words,
+// blocks in bin T -> candidate keys in this chunk's own region of the row's
+// list (LDS counter, no global atomics), then one count per chunk.
+__global__ __launch_bounds__(kThreads) void filter_kernel(
+    const int32_t* __restrict__ sel_seq_len, int32_t k, int32_t max_seq_len, WsPtrs ws) {
+  __shared__ uint32_t sh[kThreads / 64];
+  __shared__ int32_t s_T;
+  __shared__ uint32_t s_above;
+  __shared__ uint32_t s_cnt;
   const int s = blockIdx.y;
   const int c = blockIdx.x;
   const int L = min(sel_seq_len[s], max_seq_len);
   const int nb = max(L, 0) >> 2;
-  int32_t* out = topk + (size_t)s * k;
-  if (nb == 0) {
-    if (c == 0)
-      for (int i = threadIdx.x; i < k; i += kThreads) out[i] = -1;
-    return;
-  }
   const int nchunks = (nb + kScoreChunk - 1) / kScoreChunk;
   if (c >= nchunks) return;
-  const int T = ws.meta[2 * s + 0];
   const int l = lane_id(), w = threadIdx.x / 64;
   const int32_t* srow = ws.scores + (size_t)s * ws.nb_stride;
+  int32_t sc[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int j = c * kScoreChunk + it * kThreads + threadIdx.x;
+    sc[it] = (j < nb) ? srow[j] : 0;
+  }
+  if (threadIdx.x == 0) s_cnt = 0;
+  find_threshold<kThreads>(ws.hist + (size_t)s * kBins, (uint32_t)min(k, nb), sh, &s_T, &s_above);
+  const int T = s_T;
   uint64_t* bm = ws.bitmap + (size_t)s * (ws.nb_stride / 64);
-  uint64_t* keys = ws.keys + (size_t)s * ws.nb_stride;
-  uint32_t* ncand = &ws.ctr[4 * s + 2];
-
+  uint64_t* keys = ws.keys + (size_t)s * ws.nb_stride + (size_t)c * kScoreChunk;
+#pragma unroll
   for (int it = 0; it < kIters; ++it) {
     const int j0 = c * kScoreChunk + it * kThreads + w * 64;  // 64-aligned
     const int j = j0 + l;
     const bool valid = j < nb;
-    const int32_t score = valid ? srow[j] : 0;
-    const int bin = score_bin(score);
+    const int bin = score_bin(sc[it]);
     const bool sure = valid && bin > T;
     const bool maybe = valid && bin == T;
     const uint64_t sure_mask = __ballot(sure);
@@ -205,80 +202,128 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     if (l == 0) bm[j0 >> 6] = sure_mask;
     if (maybe_mask) {
       uint32_t basepos = 0;
-      if (l == 0) basepos = atomicAdd(ncand, (uint32_t)__popcll(maybe_mask));
+      if (l == 0) basepos = atomicAdd(&s_cnt, (uint32_t)__popcll(maybe_mask));
       basepos = __shfl(basepos, 0, 64);
-      if (maybe) {
-        const uint32_t pos = basepos + (uint32_t)__popcll(maybe_mask & ((1ull << l) - 1ull));
-        keys[pos] = cand_key(score, (uint32_t)j);
-      }
+      if (maybe) keys[basepos + (uint32_t)__popcll(maybe_mask & ((1ull << l) - 1ull))] = cand_key(sc[it], (uint32_t)j);
     }
   }
-  __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) is_last = (atomicAdd(&ws.ctr[4 * s + 1], 1u) == (uint32_t)(nchunks - 1));
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
+  if (threadIdx.x == 0) ws.ccount[(size_t)s * (ws.nb_stride / kScoreChunk) + c] = s_cnt;
+}
 
-  // ---- last workgroup of the row: resolve the threshold bin, then emit ----
+// Finalize (one workgroup per selecting row): radix-select the missing blocks
+// among the threshold-bin candidates, set their bits, emit ascending ids.
+constexpr int kFinThreads = 512;
+constexpr int kCandLds = 4096;
+
+__global__ __launch_bounds__(kFinThreads) void finalize_kernel(
+    const int32_t* __restrict__ sel_seq_len, int32_t k, int32_t max_seq_len,
+    int32_t* __restrict__ topk, WsPtrs ws) {
+  __shared__ uint32_t sh[kFinThreads / 64];
+  __shared__ uint32_t rhist[256];
+  __shared__ uint64_t cand[kCandLds];
+  __shared__ int32_t s_T;
+  __shared__ uint32_t s_above;
+  __shared__ uint32_t s_info[3];
+  __shared__ uint32_t s_off[kFinThreads];
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int L = min(sel_seq_len[s], max_seq_len);
+  const int nb = max(L, 0) >> 2;
+  int32_t* out = topk + (size_t)s * k;
+  if (nb == 0) {
+    for (int i = tid; i < k; i += kFinThreads) out[i] = -1;
+    return;
+  }
   const uint32_t ks = (uint32_t)min(k, nb);
-  const uint32_t n = ld_acq_u32(ncand);
-  const uint32_t need = ks - (uint32_t)ws.meta[2 * s + 1];  // 1 <= need <= n
+  uint32_t* ghist = ws.hist + (size_t)s * kBins;
+  find_threshold<kFinThreads>(ghist, ks, sh, &s_T, &s_above);
+  // Gather the chunks' candidate lists (compacted) into LDS, or into the
+  // workspace's compaction buffer when there are more than fit.
+  const int nchunks = (nb + kScoreChunk - 1) / kScoreChunk;
+  const uint32_t* ccnt = ws.ccount + (size_t)s * (ws.nb_stride / kScoreChunk);
+  const uint64_t* ckeys = ws.keys + (size_t)s * ws.nb_stride;
+  uint64_t* gkeys = ws.keys2 + (size_t)s * ws.nb_stride;
+  uint64_t* bm = ws.bitmap + (size_t)s * (ws.nb_stride / 64);
+  // Chunk offsets: one count per chunk (one round of loads), a block scan,
+  // then every candidate is copied by its own thread (a binary search over the
+  // offsets finds its chunk), so all loads of a round are in flight together.
+  uint32_t n = 0;
+  for (int c0 = 0; c0 < nchunks; c0 += kFinThreads) {
+    const int nc = min(kFinThreads, nchunks - c0);
+    const int c = c0 + tid;
+    const uint32_t cnt = (tid < nc) ? ccnt[c] : 0u;
+    const uint32_t excl = block_excl_scan<kFinThreads>(cnt, sh);
+    if (tid < nc) s_off[tid] = excl;
+    if (tid == kFinThreads - 1) s_info[0] = excl + cnt;
+    __syncthreads();
+    const uint32_t round_n = s_info[0];
+    for (uint32_t i = tid; i < round_n; i += kFinThreads) {
+      int lo = 0, hi = nc - 1;  // last chunk with s_off <= i
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= i) lo = mid; else hi = mid - 1;
+      }
+      const uint64_t key = ckeys[(size_t)(c0 + lo) * kScoreChunk + (i - s_off[lo])];
+      const uint32_t dst = n + i;
+      if (dst < (uint32_t)kCandLds) cand[dst] = key;
+      gkeys[dst] = key;
+    }
+    n += round_n;
+    __syncthreads();
+  }
+  const uint32_t need = ks - s_above;  // 1 <= need <= n
+  const bool in_lds = n <= (uint32_t)kCandLds;
+  // the histogram is consumed: clear it for the next call
+  for (int i = tid; i < kBins; i += kFinThreads) ghist[i] = 0;
+  auto key_at = [&](uint32_t i) -> uint64_t { return in_lds ? cand[i] : gkeys[i]; };
+
+  // MSB-first radix select of the need-th largest candidate key
   uint64_t prefix = 0, mask = 0;
   if (need < n) {
-    // MSB-first radix select over the 64-bit candidate keys: find the need-th
-    // largest key; all candidates share the bits of bin T, so most of the
-    // upper digits resolve in one step each.
     uint32_t rem = need;
     for (int shift = 56; shift >= 0; shift -= 8) {
-      rhist[threadIdx.x] = 0;
+      if (tid < 256) rhist[tid] = 0;
       __syncthreads();
-      for (uint32_t i = threadIdx.x; i < n; i += kThreads) {
-        const uint64_t key = ld_acq_u64(&keys[i]);
+      for (uint32_t i = tid; i < n; i += kFinThreads) {
+        const uint64_t key = key_at(i);
         if ((key & mask) == prefix) atomicAdd(&rhist[(key >> shift) & 0xff], 1u);
       }
       __syncthreads();
-      // thread t owns digit 255-t; exclusive scan gives the count of larger digits
-      const uint32_t cntd = rhist[255 - threadIdx.x];
-      uint32_t tot;
-      const uint32_t larger = block_excl_scan(cntd, sh, &tot);
-      if (larger < rem && larger + cntd >= rem) {
-        s_info[0] = 255 - threadIdx.x;
+      const uint32_t cntd = (tid < 256) ? rhist[255 - tid] : 0u;
+      const uint32_t larger = block_excl_scan<kFinThreads>(cntd, sh);
+      if (tid < 256 && larger < rem && larger + cntd >= rem) {
+        s_info[0] = 255 - tid;
         s_info[1] = larger;
         s_info[2] = cntd;
       }
       __syncthreads();
-      const uint64_t dsel = s_info[0];
       rem -= s_info[1];
-      prefix |= dsel << shift;
+      prefix |= (uint64_t)s_info[0] << shift;
       mask |= 0xffull << shift;
       const uint32_t eq = s_info[2];
       __syncthreads();
       if (eq == rem) break;  // every remaining candidate with this prefix is kept
     }
   }
-  // Mark the kept candidates: masked key > prefix, or == prefix (all of them,
-  // by construction of the early exit / exhaustion of the digits).
-  for (uint32_t i = threadIdx.x; i < n; i += kThreads) {
-    const uint64_t key = ld_acq_u64(&keys[i]);
+  for (uint32_t i = tid; i < n; i += kFinThreads) {
+    const uint64_t key = key_at(i);
     if ((key & mask) >= prefix) {
       const uint32_t j = 0xffffffffu - (uint32_t)(key & 0xffffffffull);
       atomicOr(reinterpret_cast<unsigned long long*>(&bm[j >> 6]), 1ull << (j & 63));
     }
   }
-  __threadfence();
   __syncthreads();
 
-  // Emit ascending block ids: each thread owns a contiguous run of bitmap words.
+  // emit ascending block ids: popcount prefix over the bitmap words
   const int nwords = (nb + 63) >> 6;
-  const int per = (nwords + kThreads - 1) / kThreads;
-  const int w0 = min(nwords, threadIdx.x * per), w1 = min(nwords, w0 + per);
+  const int per = (nwords + kFinThreads - 1) / kFinThreads;
+  const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
   uint32_t cntw = 0;
-  for (int i = w0; i < w1; ++i) cntw += (uint32_t)__popcll(ld_acq_u64(&bm[i]));
-  uint32_t tot;
-  uint32_t pos = block_excl_scan(cntw, sh, &tot);
+  for (int i = w0; i < w1; ++i) cntw += (uint32_t)__popcll(bm[i]);
+  uint32_t pos = block_excl_scan<kFinThreads>(cntw, sh);
   for (int i = w0; i < w1; ++i) {
-    uint64_t m = ld_acq_u64(&bm[i]);
+    uint64_t m = bm[i];
     while (m) {
       const int bit = __ffsll((long long)m) - 1;
       m &= m - 1;
@@ -286,11 +331,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       ++pos;
     }
   }
-  for (int i = (int)ks + threadIdx.x; i < k; i += kThreads) out[i] = -1;
-  if (threadIdx.x == 0) {
-    ws.ctr[4 * s + 1] = 0;
-    ws.ctr[4 * s + 2] = 0;
-  }
+  for (int i = (int)ks + tid; i < k; i += kFinThreads) out[i] = -1;
 }
 
 __global__ void clear_kernel(uint32_t* p, size_t n) {
@@ -311,9 +352,9 @@ TopkWorkspace topk_workspace_layout(int32_t rows, int32_t max_seq_len) {
   w.off_scores = off; off = al(off + (size_t)rows * w.nb_stride * 4);
   w.off_keys = off;   off = al(off + (size_t)rows * w.nb_stride * 8);
   w.off_bitmap = off; off = al(off + (size_t)rows * (w.nb_stride / 64) * 8);
+  w.off_keys2 = off;  off = al(off + (size_t)rows * w.nb_stride * 8);
   w.off_hist = off;   off = al(off + (size_t)rows * kBins * 4);
-  w.off_ctr = off;    off = al(off + (size_t)rows * 4 * 4);
-  w.off_meta = off;   off = al(off + (size_t)rows * 2 * 4);
+  w.off_ccount = off; off = al(off + (size_t)rows * (w.nb_stride / kScoreChunk) * 4);
   w.total = off;
   return w;
 }
@@ -339,9 +380,9 @@ qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len
   ws.scores = reinterpret_cast<int32_t*>(base + lay.off_scores);
   ws.keys = reinterpret_cast<uint64_t*>(base + lay.off_keys);
   ws.bitmap = reinterpret_cast<uint64_t*>(base + lay.off_bitmap);
+  ws.keys2 = reinterpret_cast<uint64_t*>(base + lay.off_keys2);
   ws.hist = reinterpret_cast<uint32_t*>(base + lay.off_hist);
-  ws.ctr = reinterpret_cast<uint32_t*>(base + lay.off_ctr);
-  ws.meta = reinterpret_cast<int32_t*>(base + lay.off_meta);
+  ws.ccount = reinterpret_cast<uint32_t*>(base + lay.off_ccount);
   ws.nb_stride = lay.nb_stride;
   const int page_log2 = __builtin_ctz((unsigned)c.page_size);
   const int chunks = lay.nb_stride / kScoreChunk;
@@ -349,27 +390,28 @@ qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len
   switch (c.index_dim) {
     case 32:
       hipLaunchKernelGGL(score_kernel<32>, grid, dim3(kThreads), 0, stream, q_index, sel_req,
-                         sel_seq_len, block_table, c.max_pages_per_req, page_log2, ckey,
-                         c.topk_blocks, max_seq_len, ws);
+                         sel_seq_len, block_table, c.max_pages_per_req, page_log2, ckey, max_seq_len, ws);
       break;
     case 64:
       hipLaunchKernelGGL(score_kernel<64>, grid, dim3(kThreads), 0, stream, q_index, sel_req,
-                         sel_seq_len, block_table, c.max_pages_per_req, page_log2, ckey,
-                         c.topk_blocks, max_seq_len, ws);
+                         sel_seq_len, block_table, c.max_pages_per_req, page_log2, ckey, max_seq_len, ws);
       break;
     case 128:
       hipLaunchKernelGGL(score_kernel<128>, grid, dim3(kThreads), 0, stream, q_index, sel_req,
-                         sel_seq_len, block_table, c.max_pages_per_req, page_log2, ckey,
-                         c.topk_blocks, max_seq_len, ws);
+                         sel_seq_len, block_table, c.max_pages_per_req, page_log2, ckey, max_seq_len, ws);
       break;
     default:
       return fail(QSA_ERR_UNSUPPORTED, "index_dim %d not built", c.index_dim);
   }
   qsa_status st = check_launch("qsa_index_topk(score)");
   if (st != QSA_OK || topk == nullptr) return st;
-  hipLaunchKernelGGL(select_kernel, grid, dim3(kThreads), 0, stream, sel_seq_len, c.topk_blocks,
+  hipLaunchKernelGGL(filter_kernel, grid, dim3(kThreads), 0, stream, sel_seq_len, c.topk_blocks,
+                     max_seq_len, ws);
+  st = check_launch("qsa_index_topk(filter)");
+  if (st != QSA_OK) return st;
+  hipLaunchKernelGGL(finalize_kernel, dim3(S), dim3(kFinThreads), 0, stream, sel_seq_len, c.topk_blocks,
                      max_seq_len, topk, ws);
-  return check_launch("qsa_index_topk(select)");
+  return check_launch("qsa_index_topk(finalize)");
 }
 
 }  // namespace qsa

@@ -20,11 +20,11 @@ struct TopkWorkspace {
   int32_t rows;        // selecting rows it is sized for
   int32_t nb_stride;   // micro-block capacity per row (multiple of the chunk)
   size_t off_scores;   // int32  [rows][nb_stride]
-  size_t off_keys;     // uint64 [rows][nb_stride]  candidates of the threshold bin
+  size_t off_keys;     // uint64 [rows][nb_stride]  threshold-bin candidates, per chunk
+  size_t off_keys2;    // uint64 [rows][nb_stride]  the same, compacted
   size_t off_bitmap;   // uint64 [rows][nb_stride/64]
-  size_t off_hist;     // uint32 [rows][kBins]
-  size_t off_ctr;      // uint32 [rows][4]: done1, done2, n_cand, pad
-  size_t off_meta;     // int32  [rows][2]: threshold bin, count strictly above it
+  size_t off_hist;     // uint32 [rows][kBins]  (all zero between calls)
+  size_t off_ccount;   // uint32 [rows][nb_stride/1024]  candidates per chunk
   size_t total;
 };
 
