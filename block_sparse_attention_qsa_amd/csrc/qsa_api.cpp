@@ -160,6 +160,8 @@ qsa_status qsa_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_
     return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_sparse_decode: NULL array argument");
   if (cfg->kv_dtype == QSA_KV_FP8_E4M3 && (!k_scale || !v_scale))
     return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_sparse_decode: fp8 K/V need k_scale and v_scale");
+  if (cfg->kv_dtype == QSA_KV_FP8_E4M3 && (!aligned(k_scale, 16) || !aligned(v_scale, 16)))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_sparse_decode: k_scale and v_scale need 16-byte alignment");
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
     return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_sparse_decode: q, k_cache, v_cache need 16-byte alignment");
   return launch_sparse_decode(*cfg, num_sel_rows, q_per_sel, num_splits, q, row_seq_len, sel_req,

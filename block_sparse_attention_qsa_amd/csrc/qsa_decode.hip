@@ -11,16 +11,21 @@
 //
 // One workgroup per (split, KV head, selecting row).  All query rows that share
 // the selection and all query heads of the GQA group are processed together
-// (NH = rows x heads-per-KV-head), so each K/V row is read from HBM once:
-//   * QK^T:  v_mfma_f32_16x16x32_bf16 with the 16 tokens of a tile as M and the
-//            NH heads as N (the group makes this dense); K goes straight from
-//            global memory into the A operand (16 B per lane).
+// (NH = rows x heads-per-KV-head), so each K/V row is read from HBM once.
+// Per tile of 16 token slots (four micro-blocks), per wave:
+//   * QK^T:  v_mfma_f32_16x16x32_bf16, M = 16 slots, N = 16 heads; K rows go
+//            straight from global memory into the A operand (16 B per lane).
 //   * softmax: online, fp32, exp2 domain; per-head running max / sum.
-//   * PV:    VALU FMAs, lane = d-pair, all NH heads per lane, so every V row is
-//            one coalesced 256 B wave load; p broadcast through LDS.
-// Four waves take interleaved tiles of 16 tokens and are merged in LDS in a
-// fixed order (deterministic).  FP8 (OCP E4M3) K/V are widened exactly to
-// bf16 / fp32; the per-token K scale multiplies the logit and the V scale
+//   * PV:    v_mfma_f32_16x16x16_bf16, M = 16 heads, N = 16 dims, K = 16 slots.
+//            The QK accumulator layout is already the PV A-operand layout, so P
+//            never leaves registers; it is split into two bf16 terms (hi + lo)
+//            to keep ~16 mantissa bits.  V is loaded as dwords (two adjacent
+//            dims) of the four rows each lane group needs and permuted into the
+//            B operand.
+// Block ids and page positions of a split are staged in LDS once; K/V loads
+// run one tile ahead.  Four waves take interleaved tiles and are merged in
+// LDS in a fixed order (deterministic).  FP8 (OCP E4M3) K/V are widened
+// exactly to bf16; the per-token K scale multiplies the logit and the V scale
 // multiplies the probability.
 #include "qsa_device.h"
 #include "qsa_internal.h"
@@ -33,12 +38,6 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // 8 fp8 E4M3 bytes -> 8 bf16 (exact: every E4M3 value is a bf16 value).
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(i32x2 w) {
@@ -79,27 +78,48 @@ constexpr int kRound = 512;  // blocks staged in LDS per round
 template <int D, bool FP8>
 struct TileLoad {
   static constexpr int KK = D / 32;
-  static constexpr int DPL = D / 64;
+  static constexpr int NPAIR = D / 32;  // pairs of 16-wide d-chunks
   i32x4 k[FP8 ? 1 : KK];   // bf16: 16 B per k-step
   i32x2 k8[FP8 ? KK : 1];  // fp8: 8 B per k-step
-  uint32_t v[16];          // this lane's V bytes of each of the 16 slots
-  int t;                   // token of slot lc (-1: none)
-  float ks, vs;            // fp8 scales of slot lc
+  uint32_t v[NPAIR][4];    // V of slots 4*lg+e at dims 32q+2lc, 32q+2lc+1
+  int tok;                 // first token of the block of slots 4*lg..4*lg+3 (-1: none)
+  f32x4 ks, vs;            // fp8 scales of those four slots
 };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4 pack4(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(s16x4, i32x2{(int)lo, (int)hi});
+}
+
+// Reductions across the four 16-lane groups with the gfx950 lane swaps (VALU, no LDS).
+__device__ __forceinline__ float max_lg(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_lg(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 template <int D, int NH, bool FP8>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
-  constexpr int NT = (NH + 15) / 16;  // MFMA N tiles of 16 heads
-  constexpr int KK = D / 32;          // MFMA k steps over the head dim
-  constexpr int DPL = D / 64;         // head-dim values per lane in PV
-  constexpr int ES = FP8 ? 1 : 2;     // bytes per K/V element
+  constexpr int NT = (NH + 15) / 16;  // MFMA tiles of 16 heads
+  constexpr int NHP = NT * 16;        // heads padded to whole tiles
+  constexpr int KK = D / 32;          // QK MFMA k steps over the head dim
+  constexpr int NPAIR = D / 32;       // PV: pairs of 16-wide d-chunks
+  constexpr int NM = D / 16;          // PV MFMAs (16-wide d-chunks) per head tile
 
-  __shared__ float p_lds[kWaves][16][NH];
-  __shared__ float alpha_lds[kWaves][NH];
-  __shared__ float ml_lds[kWaves][2][NH];
-  __shared__ float o_sh[NH][D];
-  __shared__ int32_t blk_tok[kRound];   // first token of each staged block
-  __shared__ int32_t blk_pos[kRound];   // its position in the page pool (page*page_size + slot)
+  __shared__ float ml_lds[kWaves][2][NHP];
+  __shared__ float alpha_lds[kWaves][NHP];
+  __shared__ float fac_lds[NHP][kWaves + 1];  // per-head wave factors, then 1/sum
+  __shared__ float o_w[kWaves][NH][D];        // each wave's unnormalised output
+  __shared__ int32_t blk_tok[kRound];         // first token of each staged block
+  __shared__ int32_t blk_pos[kRound];         // its position in the page pool (page*page_size + slot)
 
   const int p = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
   const int l = lane_id(), w = threadIdx.x / 64;
@@ -107,22 +127,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
   const int b = a.sel_req[s];
   const int Lsel = max(a.sel_seq_len[s], 0);
-  const int nsel = (Lsel >= 4) ? min(a.k, Lsel >> 2) : 0;
-  const int lo = (int)(((int64_t)p * nsel) / a.P);
-  const int hi = (int)(((int64_t)(p + 1) * nsel) / a.P);
-  const int nblk = hi - lo;
-  const int tail_lo = 4 * (Lsel >> 2);
   int tail_hi = 0;
   for (int i = 0; i < a.qps; ++i) tail_hi = max(tail_hi, a.row_seq_len[s * a.qps + i]);
-  const int ntailblk = (p == a.P - 1) ? (max(0, tail_hi - tail_lo) + 3) >> 2 : 0;
-  const int nall = nblk + ntailblk;  // blocks of this split (selected, then tail)
-  const int page_size = 1 << a.page_log2;
-  const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
-  const int32_t* sel = a.topk + (size_t)s * a.k + lo;
-
-  // Q as the MFMA B operand: lane (lc, lg) holds head n = nt*16+lc, dims 32kk+8lg..+8.
+  // Q as the QK MFMA B operand: lane (lc, lg) holds head n = nt*16+lc, dims 32kk+8lg..+8.
   bf16x8 bq[NT][KK];
-  int rlen[NT];  // context length of the row owning head n (C layout)
+  int rlen[NT];  // context length of the row owning head nt*16+lc
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int n = nt * 16 + lc;
@@ -137,18 +146,33 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       bq[nt][kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  const int nsel = (Lsel >= 4) ? min(a.k, Lsel >> 2) : 0;
+  const int lo = (int)(((int64_t)p * nsel) / a.P);
+  const int hi = (int)(((int64_t)(p + 1) * nsel) / a.P);
+  const int nblk = hi - lo;
+  const int tail_lo = 4 * (Lsel >> 2);
+  const int ntailblk = (p == a.P - 1) ? (max(0, tail_hi - tail_lo) + 3) >> 2 : 0;
+  const int nall = nblk + ntailblk;  // blocks of this split (selected, then tail)
+  const int page_size = 1 << a.page_log2;
+  const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
+  const int32_t* sel = a.topk + (size_t)s * a.k + lo;
 
   float m_run[NT], l_run[NT];
+  // O in the MFMA C layout: acc[nt][m][e] = O[head nt*16+4lg+e][d = 32(m/2) + 2lc + m%2]
+  f32x4 acc[NT][NM];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.f; }
-  float o[NH][DPL];
+  for (int nt = 0; nt < NT; ++nt) {
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
 #pragma unroll
-  for (int n = 0; n < NH; ++n)
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) o[n][j] = 0.f;
+    for (int m = 0; m < NM; ++m) acc[nt][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const char* kbase = reinterpret_cast<const char*>(a.k_cache);
   const char* vbase = reinterpret_cast<const char*>(a.v_cache);
+  auto row_of = [&](int pos) {  // token row inside the cache for this KV head
+    return (((pos >> a.page_log2) * a.Hkv + kvh) << a.page_log2) | (pos & (page_size - 1));
+  };
 
   for (int r0 = 0; r0 < nall; r0 += kRound) {
     const int nr = min(kRound, nall - r0);
@@ -170,34 +194,37 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     __syncthreads();
     const int ntiles = (nr + 3) >> 2;
 
-    // Slot lc of tile ti: block 4*ti + lc/4 of the round, token offset lc%4.
+    // Tile ti = blocks 4ti..4ti+3 of the round.  The A operand (K) of lane
+    // (lc, lg) is slot lc = token lc%4 of block 4ti + lc/4; its C-layout slots
+    // 4lg..4lg+3 (scores, V rows, scales) are the four tokens of block 4ti + lg.
+    // Slots without a token read row 0 of the cache (a valid address) and are masked.
     auto issue = [&](int ti, TileLoad<D, FP8>& tl) {
-      const int bi = 4 * ti + (lc >> 2);
-      int t = -1, pos = 0;
-      if (bi < nr) {
-        const int tok = blk_tok[bi];
-        if (tok >= 0) { t = tok + (lc & 3); pos = blk_pos[bi] + (lc & 3); }
-      }
-      // slots without a token read row 0 of the cache (a valid address) and are masked
-      const int row = (t >= 0) ? ((((pos >> a.page_log2) * a.Hkv + kvh) << a.page_log2) | (pos & (page_size - 1))) : 0;
-      tl.t = t;
+      const int ba = 4 * ti + (lc >> 2), bc = 4 * ti + lg;
+      const int tok_a = (ba < nr) ? blk_tok[ba] : -1;
+      const int pos_a = (ba < nr) ? blk_pos[ba] : 0;
+      const int tok_c = (bc < nr) ? blk_tok[bc] : -1;
+      const int pos_c = (bc < nr) ? blk_pos[bc] : 0;
+      const int row_a = (tok_a >= 0) ? row_of(pos_a) + (lc & 3) : 0;
+      const int row_c = (tok_c >= 0) ? row_of(pos_c) : 0;
+      tl.tok = tok_c;
       if (FP8) {
-        tl.ks = a.k_scale[pos];
-        tl.vs = a.v_scale[pos];
+        tl.ks = *reinterpret_cast<const f32x4*>(a.k_scale + (tok_c >= 0 ? pos_c : 0));
+        tl.vs = *reinterpret_cast<const f32x4*>(a.v_scale + (tok_c >= 0 ? pos_c : 0));
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-          tl.k8[kk] = *reinterpret_cast<const i32x2*>(kbase + (size_t)row * D + 32 * kk + 8 * lg);
+          tl.k8[kk] = *reinterpret_cast<const i32x2*>(kbase + (size_t)row_a * D + 32 * kk + 8 * lg);
       } else {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) tl.k[kk] = ld16(kbase + ((size_t)row * D + 32 * kk + 8 * lg) * 2);
+        for (int kk = 0; kk < KK; ++kk) tl.k[kk] = ld16(kbase + ((size_t)row_a * D + 32 * kk + 8 * lg) * 2);
       }
 #pragma unroll
-      for (int uu = 0; uu < 16; ++uu) {
-        const int r = __builtin_amdgcn_readlane(row, uu);
-        const char* vp = vbase + ((size_t)r * D + (size_t)l * DPL) * ES;
-        if (ES * DPL == 4) tl.v[uu] = *reinterpret_cast<const uint32_t*>(vp);
-        else if (ES * DPL == 2) tl.v[uu] = *reinterpret_cast<const uint16_t*>(vp);
-        else tl.v[uu] = *reinterpret_cast<const uint8_t*>(vp);
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int q = 0; q < NPAIR; ++q) {
+          const size_t el = (size_t)(row_c + (tok_c >= 0 ? e : 0)) * D + 32 * q + 2 * lc;
+          if (FP8) tl.v[q][e] = *reinterpret_cast<const uint16_t*>(vbase + el);
+          else tl.v[q][e] = *reinterpret_cast<const uint32_t*>(vbase + el * 2);
+        }
       }
     };
 
@@ -206,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     if (ti < ntiles) issue(ti, cur);
     for (; ti < ntiles; ti += kWaves) {
       if (ti + kWaves < ntiles) issue(ti + kWaves, nxt);
-      // ---- S^T = K Q^T ----
+      // ---- S^T = K Q^T  (M = 16 token slots, N = 16 heads) ----
       bf16x8 ak[KK];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
@@ -221,78 +248,80 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         for (int kk = 0; kk < KK; ++kk)
           c[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[kk], bq[nt][kk], c[nt], 0, 0, 0);
       }
-      // C layout: lane (lc, lg) holds slots 4*lg+e (e<4) for head nt*16+lc.
-      int tc[4];
-      float ksc[4], vsc[4];
+      // V operand (B: K = 16 slots, N = 16 dims): lane (lc, lg) holds slots 4lg..4lg+3
+      // of dim 32q + 2lc + h for chunk m = 2q + h.
+      s16x4 bv[NM];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        tc[e] = __shfl(cur.t, 4 * lg + e, 64);
-        if (FP8) { ksc[e] = __shfl(cur.ks, 4 * lg + e, 64); vsc[e] = __shfl(cur.vs, 4 * lg + e, 64); }
+      for (int q = 0; q < NPAIR; ++q) {
+        uint32_t w0 = cur.v[q][0], w1 = cur.v[q][1], w2 = cur.v[q][2], w3 = cur.v[q][3];
+        if (FP8) {  // two e4m3 bytes -> two bf16 (exact) per slot
+          auto cv = [](uint32_t x) -> uint32_t {
+            auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, false);
+            return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+          };
+          w0 = cv(w0); w1 = cv(w1); w2 = cv(w2); w3 = cv(w3);
+        }
+        bv[2 * q + 0] = pack4(__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u));
+        bv[2 * q + 1] = pack4(__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u));
       }
+      float pe[NT][4];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         float z[4];
         float mt = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool ok = tc[e] >= 0 && tc[e] < rlen[nt];
+          const int t = cur.tok + e;
+          const bool ok = cur.tok >= 0 && t < rlen[nt];
           float zz = c[nt][e] * a.scale_log2;
-          if (FP8) zz *= ksc[e];
+          if (FP8) zz *= cur.ks[e];
           z[e] = ok ? zz : -INFINITY;
           mt = fmaxf(mt, z[e]);
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        mt = max_lg(mt);
         const float m_new = fmaxf(m_run[nt], mt);
         float alpha, ps = 0.f;
-        float pe[4];
         if (m_new == -INFINITY) {
           alpha = 1.f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pe[e] = 0.f;
+          for (int e = 0; e < 4; ++e) pe[nt][e] = 0.f;
         } else {
           alpha = exp2f(m_run[nt] - m_new);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) { pe[e] = exp2f(z[e] - m_new); ps += pe[e]; }
+          for (int e = 0; e < 4; ++e) { pe[nt][e] = exp2f(z[e] - m_new); ps += pe[nt][e]; }
         }
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
+        ps = sum_lg(ps);
         l_run[nt] = l_run[nt] * alpha + ps;
         m_run[nt] = m_new;
-        const int n = nt * 16 + lc;
-        if (n < NH) {
+        if (lg == 0) alpha_lds[w][nt * 16 + lc] = alpha;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-          for (int e = 0; e < 4; ++e) p_lds[w][4 * lg + e][n] = FP8 ? pe[e] * vsc[e] : pe[e];
-          if (lg == 0) alpha_lds[w][n] = alpha;
+      for (int nt = 0; nt < NT; ++nt) {
+        // P as the PV A operand (M = 16 heads, K = 16 slots): exactly this C layout.
+        // Split p = hi + lo (two bf16) so the product keeps ~16 mantissa bits.
+        uint32_t ph[2], pl[2];
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          float x0 = pe[nt][2 * e2], x1 = pe[nt][2 * e2 + 1];
+          if (FP8) { x0 *= cur.vs[2 * e2]; x1 *= cur.vs[2 * e2 + 1]; }
+          const __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
+          const __bf16 l0 = (__bf16)(x0 - (float)h0), l1 = (__bf16)(x1 - (float)h1);
+          ph[e2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+          pl[e2] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+        }
+        const s16x4 aph = pack4(ph[0], ph[1]), apl = pack4(pl[0], pl[1]);
+        // rescale accumulator rows (heads 4lg+e) by their alpha
+        const f32x4 al = *reinterpret_cast<const f32x4*>(&alpha_lds[w][nt * 16 + 4 * lg]);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          acc[nt][m] *= al;
+          acc[nt][m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aph, bv[m], acc[nt][m], 0, 0, 0);
+          acc[nt][m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(apl, bv[m], acc[nt][m], 0, 0, 0);
         }
       }
-      wave_sync_lds();
-      // ---- O = alpha O + P V ----
-#pragma unroll
-      for (int n = 0; n < NH; ++n) {
-        const float al = alpha_lds[w][n];
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) o[n][j] *= al;
-      }
-#pragma unroll
-      for (int uu = 0; uu < 16; ++uu) {
-        float vf[DPL];
-        if (FP8) {
-          auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)cur.v[uu], false);
-#pragma unroll
-          for (int j = 0; j < DPL; ++j) vf[j] = f[j];
-        } else {
-#pragma unroll
-          for (int j = 0; j < DPL; ++j) vf[j] = bf16_bits_to_f32((cur.v[uu] >> (16 * j)) & 0xffffu);
-        }
-#pragma unroll
-        for (int n = 0; n < NH; ++n) {
-          const float pn = p_lds[w][uu][n];
-#pragma unroll
-          for (int j = 0; j < DPL; ++j) o[n][j] = fmaf(pn, vf[j], o[n][j]);
-        }
-      }
-      wave_sync_lds();
       cur = nxt;
     }
   }
@@ -300,47 +329,47 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // ---- merge the four waves (fixed order => deterministic) ----
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int n = nt * 16 + lc;
-    if (n < NH && lg == 0) { ml_lds[w][0][n] = m_run[nt]; ml_lds[w][1][n] = l_run[nt]; }
-  }
-  __syncthreads();
-  for (int ww = 0; ww < kWaves; ++ww) {
-    if (w == ww) {
+    if (lg == 0) { ml_lds[w][0][nt * 16 + lc] = m_run[nt]; ml_lds[w][1][nt * 16 + lc] = l_run[nt]; }
 #pragma unroll
-      for (int n = 0; n < NH; ++n) {
-        float M = -INFINITY;
+    for (int e = 0; e < 4; ++e) {
+      const int n = nt * 16 + 4 * lg + e;
+      if (n < NH) {
 #pragma unroll
-        for (int x = 0; x < kWaves; ++x) M = fmaxf(M, ml_lds[x][0][n]);
-        const float mw = ml_lds[w][0][n];
-        const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) {
-          const float val = o[n][j] * f;
-          if (ww == 0) o_sh[n][l * DPL + j] = val;
-          else o_sh[n][l * DPL + j] += val;
-        }
+        for (int q = 0; q < NPAIR; ++q)
+          *reinterpret_cast<float2*>(&o_w[w][n][32 * q + 2 * lc]) = float2{acc[nt][2 * q][e], acc[nt][2 * q + 1][e]};
       }
     }
-    __syncthreads();
   }
-  for (int idx = threadIdx.x; idx < a.nh * D; idx += kThreads) {
-    const int n = idx / D, d = idx % D;
+  __syncthreads();
+  if (threadIdx.x < NHP) {
+    const int n = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
     for (int x = 0; x < kWaves; ++x) M = fmaxf(M, ml_lds[x][0][n]);
     float Ls = 0.f;
-    if (M != -INFINITY) {
 #pragma unroll
-      for (int x = 0; x < kWaves; ++x) {
-        const float mw = ml_lds[x][0][n];
-        Ls += (mw == -INFINITY) ? 0.f : ml_lds[x][1][n] * exp2f(mw - M);
-      }
+    for (int x = 0; x < kWaves; ++x) {
+      const float mw = ml_lds[x][0][n];
+      const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      fac_lds[n][x] = f;
+      Ls += ml_lds[x][1][n] * f;
     }
+    fac_lds[n][kWaves] = (Ls > 0.f) ? 1.f / Ls : 0.f;
+    if (n < a.nh) {
+      const int r = s * a.qps + n / a.G;
+      const int h = kvh * a.G + n % a.G;
+      a.lse_part[((size_t)p * a.R + r) * a.Hq + h] = (Ls > 0.f) ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < a.nh * D; idx += kThreads) {
+    const int n = idx / D, d = idx % D;
+    float v = 0.f;
+#pragma unroll
+    for (int x = 0; x < kWaves; ++x) v += o_w[x][n][d] * fac_lds[n][x];
     const int r = s * a.qps + n / a.G;
     const int h = kvh * a.G + n % a.G;
-    const size_t orow = ((size_t)p * a.R + r) * a.Hq + h;
-    a.o_part[orow * D + d] = (Ls > 0.f) ? o_sh[n][d] / Ls : 0.f;
-    if (d == 0) a.lse_part[orow] = (Ls > 0.f) ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+    a.o_part[(((size_t)p * a.R + r) * a.Hq + h) * D + d] = v * fac_lds[n][kWaves];
   }
 }
 

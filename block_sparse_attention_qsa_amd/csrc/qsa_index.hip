@@ -40,6 +40,7 @@ struct WsPtrs {
   uint64_t* keys2;
   uint32_t* hist;
   uint32_t* ccount;
+  int32_t* meta;
   int32_t nb_stride;
 };
 
@@ -208,24 +209,29 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) ws.ccount[(size_t)s * (ws.nb_stride / kScoreChunk) + c] = s_cnt;
+  if (threadIdx.x == 0) {
+    ws.ccount[(size_t)s * (ws.nb_stride / kScoreChunk) + c] = s_cnt;
+    if (c == 0) { ws.meta[2 * s] = T; ws.meta[2 * s + 1] = (int32_t)s_above; }
+  }
 }
 
 // Finalize (one workgroup per selecting row): radix-select the missing blocks
 // among the threshold-bin candidates, set their bits, emit ascending ids.
 constexpr int kFinThreads = 512;
-constexpr int kCandLds = 4096;
+constexpr int kCandLds = 4096;   // candidates held in LDS (more: workspace)
+constexpr int kWordsLds = 4096;  // bitmap words held in LDS (rows up to 262,144 blocks)
+constexpr int kSpec = 8;         // candidate keys per chunk loaded with the counts
 
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     const int32_t* __restrict__ sel_seq_len, int32_t k, int32_t max_seq_len,
     int32_t* __restrict__ topk, WsPtrs ws) {
   __shared__ uint32_t sh[kFinThreads / 64];
-  __shared__ uint32_t rhist[256];
+  __shared__ __align__(16) uint32_t rhist[256];
   __shared__ uint64_t cand[kCandLds];
-  __shared__ int32_t s_T;
-  __shared__ uint32_t s_above;
+  __shared__ uint64_t bml[kWordsLds];
   __shared__ uint32_t s_info[3];
   __shared__ uint32_t s_off[kFinThreads];
+  __shared__ uint64_t s_sel[2];
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
   const int L = min(sel_seq_len[s], max_seq_len);
@@ -236,94 +242,135 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     return;
   }
   const uint32_t ks = (uint32_t)min(k, nb);
-  uint32_t* ghist = ws.hist + (size_t)s * kBins;
-  find_threshold<kFinThreads>(ghist, ks, sh, &s_T, &s_above);
-  // Gather the chunks' candidate lists (compacted) into LDS, or into the
-  // workspace's compaction buffer when there are more than fit.
   const int nchunks = (nb + kScoreChunk - 1) / kScoreChunk;
+  const int nwords = (nb + 63) >> 6;
+  const bool bm_lds = nwords <= kWordsLds;
+  uint32_t* ghist = ws.hist + (size_t)s * kBins;
   const uint32_t* ccnt = ws.ccount + (size_t)s * (ws.nb_stride / kScoreChunk);
   const uint64_t* ckeys = ws.keys + (size_t)s * ws.nb_stride;
   uint64_t* gkeys = ws.keys2 + (size_t)s * ws.nb_stride;
   uint64_t* bm = ws.bitmap + (size_t)s * (ws.nb_stride / 64);
-  // Chunk offsets: one count per chunk (one round of loads), a block scan,
-  // then every candidate is copied by its own thread (a binary search over the
-  // offsets finds its chunk), so all loads of a round are in flight together.
+
+  // The filter's bitmap of blocks above the threshold bin (into LDS), the
+  // count of blocks above the threshold bin, and per chunk the candidate
+  // count plus its first kSpec candidate keys: one round of loads.
+  if (bm_lds)
+    for (int i = tid; i < nwords; i += kFinThreads) bml[i] = bm[i];
+  const uint32_t above = (uint32_t)ws.meta[2 * s + 1];
   uint32_t n = 0;
   for (int c0 = 0; c0 < nchunks; c0 += kFinThreads) {
     const int nc = min(kFinThreads, nchunks - c0);
-    const int c = c0 + tid;
-    const uint32_t cnt = (tid < nc) ? ccnt[c] : 0u;
+    uint32_t cnt = 0;
+    uint64_t spec[kSpec];
+    if (tid < nc) {
+      cnt = ccnt[c0 + tid];
+      const uint64_t* src = ckeys + (size_t)(c0 + tid) * kScoreChunk;
+#pragma unroll
+      for (int i = 0; i < kSpec; ++i) spec[i] = src[i];
+    }
     const uint32_t excl = block_excl_scan<kFinThreads>(cnt, sh);
     if (tid < nc) s_off[tid] = excl;
     if (tid == kFinThreads - 1) s_info[0] = excl + cnt;
+#pragma unroll
+    for (int i = 0; i < kSpec; ++i) {
+      const uint32_t dst = n + excl + i;
+      if ((uint32_t)i < cnt) {
+        if (dst < (uint32_t)kCandLds) cand[dst] = spec[i];
+        else gkeys[dst] = spec[i];
+      }
+    }
     __syncthreads();
     const uint32_t round_n = s_info[0];
+    // chunks with more than kSpec candidates: copy the rest, one thread each
     for (uint32_t i = tid; i < round_n; i += kFinThreads) {
       int lo = 0, hi = nc - 1;  // last chunk with s_off <= i
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (s_off[mid] <= i) lo = mid; else hi = mid - 1;
       }
-      const uint64_t key = ckeys[(size_t)(c0 + lo) * kScoreChunk + (i - s_off[lo])];
+      const uint32_t r = i - s_off[lo];
+      if (r < (uint32_t)kSpec) continue;
+      const uint64_t key = ckeys[(size_t)(c0 + lo) * kScoreChunk + r];
       const uint32_t dst = n + i;
       if (dst < (uint32_t)kCandLds) cand[dst] = key;
-      gkeys[dst] = key;
+      else gkeys[dst] = key;
     }
     n += round_n;
     __syncthreads();
   }
-  const uint32_t need = ks - s_above;  // 1 <= need <= n
-  const bool in_lds = n <= (uint32_t)kCandLds;
-  // the histogram is consumed: clear it for the next call
+  // the row histogram is consumed (the filter used it): clear it for the next call
   for (int i = tid; i < kBins; i += kFinThreads) ghist[i] = 0;
-  auto key_at = [&](uint32_t i) -> uint64_t { return in_lds ? cand[i] : gkeys[i]; };
+  const uint32_t need = ks - above;  // 1 <= need <= n
+  auto key_at = [&](uint32_t i) -> uint64_t { return i < (uint32_t)kCandLds ? cand[i] : gkeys[i]; };
 
-  // MSB-first radix select of the need-th largest candidate key
-  uint64_t prefix = 0, mask = 0;
-  if (need < n) {
+  // MSB-first radix select of the need-th largest candidate key, by wave 0
+  // alone (no workgroup barriers inside).  All candidates share the threshold
+  // bin, i.e. key bits 46..63, so the digits start at bit 40.
+  constexpr uint64_t kBinMask = ~((1ull << (32 + kBinShift)) - 1ull);
+  if (tid < 64 && need < n) {
+    const int l = tid;
+    auto wave_lds_sync = []() {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    uint64_t mask = kBinMask, prefix = key_at(0) & kBinMask;
     uint32_t rem = need;
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      if (tid < 256) rhist[tid] = 0;
-      __syncthreads();
-      for (uint32_t i = tid; i < n; i += kFinThreads) {
+    for (int shift = 40; shift >= 0; shift -= 8) {
+      *reinterpret_cast<uint4*>(&rhist[4 * l]) = uint4{0u, 0u, 0u, 0u};
+      wave_lds_sync();
+      for (uint32_t i = l; i < n; i += 64) {
         const uint64_t key = key_at(i);
         if ((key & mask) == prefix) atomicAdd(&rhist[(key >> shift) & 0xff], 1u);
       }
-      __syncthreads();
-      const uint32_t cntd = (tid < 256) ? rhist[255 - tid] : 0u;
-      const uint32_t larger = block_excl_scan<kFinThreads>(cntd, sh);
-      if (tid < 256 && larger < rem && larger + cntd >= rem) {
-        s_info[0] = 255 - tid;
-        s_info[1] = larger;
-        s_info[2] = cntd;
+      wave_lds_sync();
+      // lane l owns digits 255-4l .. 252-4l (descending)
+      const uint4 hv = *reinterpret_cast<const uint4*>(&rhist[252 - 4 * l]);
+      const uint32_t cs[4] = {hv.w, hv.z, hv.y, hv.x};
+      const uint32_t tot = cs[0] + cs[1] + cs[2] + cs[3];
+      uint32_t acc = wave_incl_scan(tot) - tot;  // count in larger digits
+      uint32_t dsel = 0, larger = 0, cnt = 0;
+      bool mine = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!mine && acc < rem && acc + cs[i] >= rem) { mine = true; dsel = 255 - 4 * l - i; larger = acc; cnt = cs[i]; }
+        acc += cs[i];
       }
-      __syncthreads();
-      rem -= s_info[1];
-      prefix |= (uint64_t)s_info[0] << shift;
+      const int src = __ffsll((long long)__ballot(mine)) - 1;
+      dsel = __shfl(dsel, src, 64);
+      larger = __shfl(larger, src, 64);
+      cnt = __shfl(cnt, src, 64);
+      rem -= larger;
+      prefix = (prefix & ~(0xffull << shift)) | ((uint64_t)dsel << shift);
       mask |= 0xffull << shift;
-      const uint32_t eq = s_info[2];
-      __syncthreads();
-      if (eq == rem) break;  // every remaining candidate with this prefix is kept
+      wave_lds_sync();
+      if (cnt == rem) break;  // every remaining candidate with this prefix is kept
     }
+    if (l == 0) { s_sel[0] = prefix; s_sel[1] = mask; }
+  } else if (tid == 0) {
+    s_sel[0] = 0;  // keep every candidate
+    s_sel[1] = 0;
   }
+  __syncthreads();
+  const uint64_t prefix = s_sel[0], mask = s_sel[1];
   for (uint32_t i = tid; i < n; i += kFinThreads) {
     const uint64_t key = key_at(i);
     if ((key & mask) >= prefix) {
       const uint32_t j = 0xffffffffu - (uint32_t)(key & 0xffffffffull);
-      atomicOr(reinterpret_cast<unsigned long long*>(&bm[j >> 6]), 1ull << (j & 63));
+      if (bm_lds) atomicOr(reinterpret_cast<unsigned long long*>(&bml[j >> 6]), 1ull << (j & 63));
+      else atomicOr(reinterpret_cast<unsigned long long*>(&bm[j >> 6]), 1ull << (j & 63));
     }
   }
   __syncthreads();
 
   // emit ascending block ids: popcount prefix over the bitmap words
-  const int nwords = (nb + 63) >> 6;
   const int per = (nwords + kFinThreads - 1) / kFinThreads;
   const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
   uint32_t cntw = 0;
-  for (int i = w0; i < w1; ++i) cntw += (uint32_t)__popcll(bm[i]);
+  for (int i = w0; i < w1; ++i) cntw += (uint32_t)__popcll(bm_lds ? bml[i] : bm[i]);
   uint32_t pos = block_excl_scan<kFinThreads>(cntw, sh);
   for (int i = w0; i < w1; ++i) {
-    uint64_t m = bm[i];
+    uint64_t m = bm_lds ? bml[i] : bm[i];
     while (m) {
       const int bit = __ffsll((long long)m) - 1;
       m &= m - 1;
@@ -355,6 +402,7 @@ TopkWorkspace topk_workspace_layout(int32_t rows, int32_t max_seq_len) {
   w.off_keys2 = off;  off = al(off + (size_t)rows * w.nb_stride * 8);
   w.off_hist = off;   off = al(off + (size_t)rows * kBins * 4);
   w.off_ccount = off; off = al(off + (size_t)rows * (w.nb_stride / kScoreChunk) * 4);
+  w.off_meta = off;   off = al(off + (size_t)rows * 2 * 4);
   w.total = off;
   return w;
 }
@@ -383,6 +431,7 @@ qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len
   ws.keys2 = reinterpret_cast<uint64_t*>(base + lay.off_keys2);
   ws.hist = reinterpret_cast<uint32_t*>(base + lay.off_hist);
   ws.ccount = reinterpret_cast<uint32_t*>(base + lay.off_ccount);
+  ws.meta = reinterpret_cast<int32_t*>(base + lay.off_meta);
   ws.nb_stride = lay.nb_stride;
   const int page_log2 = __builtin_ctz((unsigned)c.page_size);
   const int chunks = lay.nb_stride / kScoreChunk;

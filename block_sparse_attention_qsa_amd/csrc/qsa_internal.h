@@ -25,6 +25,7 @@ struct TopkWorkspace {
   size_t off_bitmap;   // uint64 [rows][nb_stride/64]
   size_t off_hist;     // uint32 [rows][kBins]  (all zero between calls)
   size_t off_ccount;   // uint32 [rows][nb_stride/1024]  candidates per chunk
+  size_t off_meta;     // int32  [rows][2]  threshold bin, count of blocks above it
   size_t total;
 };
 
