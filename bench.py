@@ -103,6 +103,21 @@ def cpu_baseline(wl, seconds: float):
                                       f"float64, one thread, {el:.1f} s"}
 
 
+def measured_traffic():
+    """HBM bytes per scan launch from the committed rocprofv3 counter summary,
+    or None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "score_kernel_long256k_hbm_counters.md")
+    try:
+        kv = dict(line.split(" = ", 1) for line in open(path).read().splitlines() if " = " in line)
+        src = os.path.join(ROOT, kv["kernel_source"].strip())
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["kernel_source_sha256"].strip():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def copy_calibration(mib: int):
     """A plain device copy of known size (for scaling rocprofv3 byte counters)."""
     import torch
@@ -256,7 +271,8 @@ def main():
                      "wall_s": t_wall},
         "roofline": {"kernel": "qsa::score_kernel (qsa_index_topk compressed-key scan)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic() if cfg == 3 else None,
                      "bytes_per_launch": scan_per_launch, "avg_launch_us": kern_ms * 1e3,
                      "launches_timed": n_launches},
     }
