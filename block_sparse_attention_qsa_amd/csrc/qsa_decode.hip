@@ -374,16 +374,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 }
 
 // ---- merge: one wave per (row, head) ----
+// The partials' LSEs and outputs are loaded in one round (16 partials at a
+// time), then reduced: lane p holds lse_p; the outputs are weighted by
+// exp(lse_p - lse) broadcast from lane p.
 template <int D, typename OutT>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_part,
                                                     const float* __restrict__ lse_part,
                                                     OutT* __restrict__ out, float* __restrict__ lse,
                                                     int32_t P, int32_t RH) {
   constexpr int DPL = D / 64;
+  constexpr int CH = 16;
   const int l = lane_id();
   const int rh = blockIdx.x * 4 + threadIdx.x / 64;
   if (rh >= RH) return;
-  float lp = (l < P) ? lse_part[(size_t)l * RH + rh] : -INFINITY;
+  const float lp = (l < P) ? lse_part[(size_t)l * RH + rh] : -INFINITY;
+  float v[CH][DPL];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const float* src = o_part + ((size_t)min(i, P - 1) * RH + rh) * D + l * DPL;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) v[i][j] = src[j];
+  }
   const float M = wave_max(lp);
   float acc[DPL];
 #pragma unroll
@@ -395,13 +406,26 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
     const float sum = wave_sum(wgt);
     if (l == 0) lse[rh] = M + logf(sum);
     const float inv = 1.f / sum;
-#pragma unroll 8
-    for (int pp = 0; pp < P; ++pp) {
-      // empty partials have weight 0 and finite (zero) outputs: no branch
-      const float wp = __shfl(wgt, pp, 64) * inv;
-      const float* src = o_part + ((size_t)pp * RH + rh) * D + l * DPL;
+    // empty partials have weight 0 and finite (zero) outputs
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) acc[j] = fmaf(wp, src[j], acc[j]);
+    for (int i = 0; i < CH; ++i) {
+      const float wp = (i < P) ? __shfl(wgt, i, 64) * inv : 0.f;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) acc[j] = fmaf(wp, v[i][j], acc[j]);
+    }
+    for (int p0 = CH; p0 < P; p0 += CH) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const float* src = o_part + ((size_t)min(p0 + i, P - 1) * RH + rh) * D + l * DPL;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) v[i][j] = src[j];
+      }
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const float wp = (p0 + i < P) ? __shfl(wgt, p0 + i, 64) * inv : 0.f;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) acc[j] = fmaf(wp, v[i][j], acc[j]);
+      }
     }
   }
 #pragma unroll

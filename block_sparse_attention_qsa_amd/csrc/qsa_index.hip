@@ -30,8 +30,10 @@ namespace qsa {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;                          // filter kernel
 constexpr int kIters = kScoreChunk / kThreads;
+constexpr int kScoreThreads = 512;                     // score kernel
+constexpr int kScoreIters = kScoreChunk / kScoreThreads;
 
 struct WsPtrs {
   int32_t* scores;
@@ -53,10 +55,10 @@ __device__ __forceinline__ uint64_t cand_key(int32_t score, uint32_t j) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void score_kernel(
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(
     const int8_t* __restrict__ q_index, const int32_t* __restrict__ sel_req,
     const int32_t* __restrict__ sel_seq_len, const int32_t* __restrict__ block_table,
-    int32_t max_pages, int32_t page_log2, const int8_t* __restrict__ ckey,
+    int32_t max_pages, int32_t page_log2, const int8_t* ckey,
     int32_t max_seq_len, WsPtrs ws) {
   __shared__ uint32_t hist[kBins];
   const int s = blockIdx.y;
@@ -70,16 +72,24 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
   const int bpp = 1 << bpp_log2;
   const size_t page_bytes = (size_t)bpp * 2 * D;
 
-  for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0;
+  // Clear the LDS histogram before any global load is in flight: a barrier
+  // waits for every outstanding load, so none may sit between the loads and
+  // the arithmetic (that would serialise the whole stream before any scoring).
+  for (int i = threadIdx.x; i < kBins; i += kScoreThreads) hist[i] = 0;
+  __syncthreads();
 
-  // Page ids of this thread's kIters blocks first (one round trip), then all
-  // compressed-key loads at once, then the arithmetic.
+  // Page ids of this thread's kScoreIters blocks first (one round trip), then all
+  // compressed-key loads at once; each block is scored as soon as its loads
+  // have arrived, while the later ones are still in flight.
+  // Loads are unconditional (past the row's end they re-read its last block and
+  // the result is dropped): a guarded load becomes a branch, and the compiler
+  // then drains all outstanding loads at every branch.
   const int32_t* bt = block_table + (size_t)b * max_pages;
-  int page[kIters];
+  int page[kScoreIters];
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int j = c * kScoreChunk + it * kThreads + threadIdx.x;
-    page[it] = (j < nb) ? bt[j >> bpp_log2] : 0;
+  for (int it = 0; it < kScoreIters; ++it) {
+    const int j = min(c * kScoreChunk + it * kScoreThreads + (int)threadIdx.x, nb - 1);
+    page[it] = bt[j >> bpp_log2];
   }
   // indexer query: D int8 = D/4 packed dwords, uniform across the workgroup
   int32_t qw[D / 4];
@@ -87,20 +97,19 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
 #pragma unroll
   for (int i = 0; i < D / 4; ++i) qw[i] = q32[i];
 
-  i32x4 v[kIters][D / 8];
+  i32x4 v[kScoreIters][D / 8];
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int j = c * kScoreChunk + it * kThreads + threadIdx.x;
+  for (int it = 0; it < kScoreIters; ++it) {
+    const int j = min(c * kScoreChunk + it * kScoreThreads + (int)threadIdx.x, nb - 1);
     const int8_t* base = ckey + (size_t)page[it] * page_bytes + (size_t)(j & (bpp - 1)) * 16;
 #pragma unroll
-    for (int ch = 0; ch < D / 8; ++ch)
-      v[it][ch] = (j < nb) ? ld16(base + (size_t)ch * bpp * 16) : i32x4{0, 0, 0, 0};
+    for (int ch = 0; ch < D / 8; ++ch)  // streamed once: non-temporal
+      v[it][ch] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(base + (size_t)ch * bpp * 16));
   }
-  __syncthreads();  // hist cleared
   int32_t* srow = ws.scores + (size_t)s * ws.nb_stride;
+  int32_t sc[kScoreIters];
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int j = c * kScoreChunk + it * kThreads + threadIdx.x;
+  for (int it = 0; it < kScoreIters; ++it) {
     int32_t lo = 0, hi = 0;
 #pragma unroll
     for (int ch = 0; ch < D / 16; ++ch) {
@@ -110,17 +119,22 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
         hi = __builtin_amdgcn_sdot4(v[it][ch + D / 16][e], qw[4 * ch + e], hi, false);
       }
     }
-    const int32_t score = lo + hi * 256;
-    if (j < nb) {
-      srow[j] = score;
-      atomicAdd(&hist[score_bin(score)], 1u);
-    }
+    sc[it] = lo + hi * 256;
+  }
+  // No branches here either: the workspace has score slots up to the chunk's
+  // end (slots past the row's end are never read), and blocks past the end add
+  // 0 to the histogram.
+#pragma unroll
+  for (int it = 0; it < kScoreIters; ++it) {
+    const int j = c * kScoreChunk + it * kScoreThreads + threadIdx.x;
+    srow[j] = sc[it];
+    atomicAdd(&hist[score_bin(sc[it])], j < nb ? 1u : 0u);
   }
   __syncthreads();
   // Per-row histogram in the workspace: device-scope atomics, read by the
   // next kernel after this one has finished (no fence needed here).
   uint32_t* ghist = ws.hist + (size_t)s * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kThreads) {
+  for (int i = threadIdx.x; i < kBins; i += kScoreThreads) {
     const uint32_t h = hist[i];
     if (h) atomicAdd(&ghist[i], h);
   }
@@ -179,12 +193,9 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
   if (c >= nchunks) return;
   const int l = lane_id(), w = threadIdx.x / 64;
   const int32_t* srow = ws.scores + (size_t)s * ws.nb_stride;
-  int32_t sc[kIters];
+  int32_t sc[kIters];  // unconditional loads: slots past the row's end exist and are masked
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int j = c * kScoreChunk + it * kThreads + threadIdx.x;
-    sc[it] = (j < nb) ? srow[j] : 0;
-  }
+  for (int it = 0; it < kIters; ++it) sc[it] = srow[c * kScoreChunk + it * kThreads + threadIdx.x];
   if (threadIdx.x == 0) s_cnt = 0;
   find_threshold<kThreads>(ws.hist + (size_t)s * kBins, (uint32_t)min(k, nb), sh, &s_T, &s_above);
   const int T = s_T;
@@ -438,15 +449,15 @@ qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len
   dim3 grid(chunks, S);
   switch (c.index_dim) {
     case 32:
-      hipLaunchKernelGGL(score_kernel<32>, grid, dim3(kThreads), 0, stream, q_index, sel_req,
+      hipLaunchKernelGGL(score_kernel<32>, grid, dim3(kScoreThreads), 0, stream, q_index, sel_req,
                          sel_seq_len, block_table, c.max_pages_per_req, page_log2, ckey, max_seq_len, ws);
       break;
     case 64:
-      hipLaunchKernelGGL(score_kernel<64>, grid, dim3(kThreads), 0, stream, q_index, sel_req,
+      hipLaunchKernelGGL(score_kernel<64>, grid, dim3(kScoreThreads), 0, stream, q_index, sel_req,
                          sel_seq_len, block_table, c.max_pages_per_req, page_log2, ckey, max_seq_len, ws);
       break;
     case 128:
-      hipLaunchKernelGGL(score_kernel<128>, grid, dim3(kThreads), 0, stream, q_index, sel_req,
+      hipLaunchKernelGGL(score_kernel<128>, grid, dim3(kScoreThreads), 0, stream, q_index, sel_req,
                          sel_seq_len, block_table, c.max_pages_per_req, page_log2, ckey, max_seq_len, ws);
       break;
     default:
