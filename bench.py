@@ -49,7 +49,8 @@ def algorithmic_bytes(wl):
     """Bytes the step must move, per layer (intermediates excluded).
 
     scan: every closed micro-block of every selecting row at its stored width
-    (2 bytes per index dim), its page-table entries and the indexer query;
+    (10 bits per index dim: D + D/4 bytes), its page-table entries and the
+    indexer query;
     attend: the selected and tail K/V rows of each selecting row's request,
     read once per KV head for all rows sharing the selection (+ fp8 scales),
     q, the output (fp32) and lse.
@@ -60,7 +61,7 @@ def algorithmic_bytes(wl):
     sel_len = wl.sel_seq_len.cpu().numpy().astype(np.int64)
     row_len = wl.row_seq_len.cpu().numpy().astype(np.int64)
     nb = sel_len // 4
-    scan = int((nb * 2 * D).sum() + (((sel_len + page - 1) // page) * 4).sum() + len(sel_len) * D)
+    scan = int((nb * (D + D // 4)).sum() + (((sel_len + page - 1) // page) * 4).sum() + len(sel_len) * D)
     attend = 0
     for si in range(wl.num_sel):
         rows = row_len[si * wl.q_per_sel:(si + 1) * wl.q_per_sel]

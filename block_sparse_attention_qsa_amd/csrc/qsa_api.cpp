@@ -73,7 +73,8 @@ extern "C" {
 
 size_t qsa_ckey_cache_bytes(const qsa_config* cfg, int64_t num_pages) {
   if (check_config(cfg, true, false) != QSA_OK || num_pages < 0) return 0;
-  return (size_t)num_pages * (size_t)cfg->page_size / 4 * 2 * (size_t)cfg->index_dim;
+  // per micro-block: D bytes of the s plane + D/4 bytes of the two bit-masks
+  return (size_t)num_pages * (size_t)cfg->page_size / 4 * ((size_t)cfg->index_dim + (size_t)cfg->index_dim / 4);
 }
 
 qsa_status qsa_compress(const qsa_config* cfg, int32_t num_reqs, int32_t max_new_tokens,

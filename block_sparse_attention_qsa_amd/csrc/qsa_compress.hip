@@ -4,9 +4,12 @@
 // Method ("Qwen 4 QSA 迎来解码上下文并行" blog, section on what the pull request
 // changes; "PR #53896 完整报告", implementation breakdown): token keys enter a
 // raw-key ring and are pooled by the compress ratio (4) into the compressed key
-// cache.  Pooling here is the exact integer sum of the 4 int8 keys; it is stored
-// losslessly as two int8 planes (C = 256*hi + lo), so the scoring kernel keeps
-// using int8 dot products and stays bit-exact.
+// cache.  Pooling here is the exact integer sum of the 4 int8 keys,
+// C in [-512, 508], stored losslessly in 10 bits per dimension:
+//   v = C + 512 in [0, 1023];  s = (v mod 256) - 128 (an int8 plane);
+//   b0, b1 = bits 8 and 9 of v (two bit-masks over the dimensions),
+// so C = 256*(2*b1 + b0) + s - 384.  The scoring kernel keeps int8 dot
+// products for the s plane and adds masked sums of the query for the masks.
 //
 // Work split: one grid row (blockIdx.y) per request, workgroups stride over the
 // micro-blocks that close in this call.  Only the block that straddles the
@@ -38,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
   const int jE = (L0 + n) >> 2;                  // closing blocks are [jA, jE)
   const int bpp_log2 = page_log2 - 2;            // micro-blocks per page (log2)
   const int bpp = 1 << bpp_log2;
-  const size_t page_bytes = (size_t)bpp * 2 * D; // 16 B chunks x (2D/16) x bpp
+  const size_t page_bytes = (size_t)bpp * (D + D / 4);  // s plane + two bit-masks per block
   const int grp = threadIdx.x % kGroups;
   const int sub = threadIdx.x / kGroups;
   const int8_t* ring_b = ring + (size_t)b * kRing * D;
@@ -54,21 +57,26 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[i] += (int32_t)(int8_t)(w >> (8 * i));
     }
-    uint32_t lo = 0, hi = 0;
+    uint32_t splane = 0, m0 = 0, m1 = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int32_t l = (int32_t)(int8_t)(s[i] & 0xff);  // low byte, signed
-      const int32_t h = (s[i] - l) >> 8;                 // exact: s - l is a multiple of 256
-      lo |= (uint32_t)(l & 0xff) << (8 * i);
-      hi |= (uint32_t)(h & 0xff) << (8 * i);
+      const uint32_t v = (uint32_t)(s[i] + 512);  // 10 bits
+      splane |= ((v & 0xffu) ^ 0x80u) << (8 * i);  // (v mod 256) - 128 as int8
+      m0 |= ((v >> 8) & 1u) << i;
+      m1 |= ((v >> 9) & 1u) << i;
     }
+    // dims 8k..8k+3 (even group) and 8k+4..8k+7 (odd group) form mask byte k
+    const uint32_t m0p = __shfl_xor(m0, 1, 64), m1p = __shfl_xor(m1, 1, 64);
     const int page = block_table[(size_t)b * max_pages + (j >> bpp_log2)];
     const int slot = j & (bpp - 1);
-    int8_t* dst = ckey + (size_t)page * page_bytes + (size_t)slot * 16;
+    int8_t* pg = ckey + (size_t)page * page_bytes;
     const int byte = 4 * grp;                     // dims [4grp, 4grp+4)
-    const int chunk = byte >> 4;
-    *reinterpret_cast<uint32_t*>(dst + (size_t)chunk * bpp * 16 + (byte & 15)) = lo;
-    *reinterpret_cast<uint32_t*>(dst + (size_t)(chunk + D / 16) * bpp * 16 + (byte & 15)) = hi;
+    *reinterpret_cast<uint32_t*>(pg + (size_t)(byte >> 4) * bpp * 16 + (size_t)slot * 16 + (byte & 15)) = splane;
+    if ((grp & 1) == 0) {
+      uint8_t* mk = reinterpret_cast<uint8_t*>(pg + (size_t)(D / 16) * bpp * 16 + (size_t)slot * (D / 4));
+      mk[grp >> 1] = (uint8_t)(m0 | (m0p << 4));
+      mk[D / 8 + (grp >> 1)] = (uint8_t)(m1 | (m1p << 4));
+    }
   }
 
   if (blockIdx.x != 0) return;

@@ -10,10 +10,13 @@
 // Three kernels, no fences and no inter-workgroup waits (each kernel boundary
 // publishes the previous kernel's results):
 //   score    (grid: chunk of 1024 micro-blocks x selecting row): streams the
-//            2-byte compressed keys (the HBM-bound scan), computes
-//            score = q.lo + 256 q.hi with v_dot4_i32_i8, stores the int32 score
-//            and adds an LDS histogram of the score's top 11 bits into a
-//            per-row histogram with device-scope atomics.
+//            10-bit compressed keys (the HBM-bound scan: an int8 plane s and two
+//            bit-masks b0, b1 per block), computes
+//            score = q.s (v_dot4_i32_i8) + 256 (2 q.b1 + q.b0) - 384 sum(q),
+//            the masked sums as popcounts of the masks against the query's
+//            bit-planes (built per wave with ballots), stores
+//            the int32 score and adds an LDS histogram of the score's top 11
+//            bits into a per-row histogram with device-scope atomics.
 //   filter   (same grid): each workgroup derives the threshold bin T from the
 //            row histogram (fewer than k scores above T, at least k at or above
 //            it), writes bitmap words of its blocks above T and appends 64-bit
@@ -60,27 +63,26 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     const int32_t* __restrict__ sel_seq_len, const int32_t* __restrict__ block_table,
     int32_t max_pages, int32_t page_log2, const int8_t* ckey,
     int32_t max_seq_len, WsPtrs ws) {
+  constexpr int kSChunks = D / 16;       // 16-byte chunks of the s plane
+  constexpr int kMaskWords = D / 32;     // dwords per D-bit mask
+  constexpr int kMaskLoads = (2 * kMaskWords + 3) / 4;
   __shared__ uint32_t hist[kBins];
   const int s = blockIdx.y;
   const int c = blockIdx.x;
-  const int L = min(sel_seq_len[s], max_seq_len);
+  const int Lr = sel_seq_len[s];
+  const int b = sel_req[s];
+  // Both row loads and the argument pointers in flight together: the compiler
+  // would otherwise fetch each only after the exit test below, one wait each.
+  asm volatile("" ::"s"(Lr), "s"(b), "s"(block_table), "s"(q_index), "s"(ckey), "s"(max_pages),
+               "s"(page_log2), "s"(ws.scores), "s"(ws.hist), "s"(ws.nb_stride));
+  const int L = min(Lr, max_seq_len);
   const int nb = max(L, 0) >> 2;
   const int nchunks = (nb + kScoreChunk - 1) / kScoreChunk;
   if (c >= nchunks) return;
-  const int b = sel_req[s];
   const int bpp_log2 = page_log2 - 2;
   const int bpp = 1 << bpp_log2;
-  const size_t page_bytes = (size_t)bpp * 2 * D;
+  const size_t page_bytes = (size_t)bpp * (D + D / 4);
 
-  // Clear the LDS histogram before any global load is in flight: a barrier
-  // waits for every outstanding load, so none may sit between the loads and
-  // the arithmetic (that would serialise the whole stream before any scoring).
-  for (int i = threadIdx.x; i < kBins; i += kScoreThreads) hist[i] = 0;
-  __syncthreads();
-
-  // Page ids of this thread's kScoreIters blocks first (one round trip), then all
-  // compressed-key loads at once; each block is scored as soon as its loads
-  // have arrived, while the later ones are still in flight.
   // Loads are unconditional (past the row's end they re-read its last block and
   // the result is dropped): a guarded load becomes a branch, and the compiler
   // then drains all outstanding loads at every branch.
@@ -91,48 +93,92 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     const int j = min(c * kScoreChunk + it * kScoreThreads + (int)threadIdx.x, nb - 1);
     page[it] = bt[j >> bpp_log2];
   }
-  // indexer query: D int8 = D/4 packed dwords, uniform across the workgroup
+
+  // All key loads at once (non-temporal: streamed once); each block is scored
+  // as soon as its loads have arrived, while the later ones are still in flight.
+  i32x4 v[kScoreIters][kSChunks];
+  i32x4 mk[kScoreIters][kMaskLoads];
+#pragma unroll
+  for (int it = 0; it < kScoreIters; ++it) {
+    const int j = min(c * kScoreChunk + it * kScoreThreads + (int)threadIdx.x, nb - 1);
+    const int slot = j & (bpp - 1);
+    const int8_t* pg = ckey + (size_t)page[it] * page_bytes;
+#pragma unroll
+    for (int ch = 0; ch < kSChunks; ++ch)
+      v[it][ch] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pg + (size_t)ch * bpp * 16 + (size_t)slot * 16));
+    const int8_t* mp = pg + (size_t)kSChunks * bpp * 16 + (size_t)slot * (D / 4);
+    if (D >= 64) {
+#pragma unroll
+      for (int m = 0; m < kMaskLoads; ++m)
+        mk[it][m] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(mp + 16 * m));
+    } else {  // D = 32: 8 mask bytes
+      const i32x2 m2 = __builtin_nontemporal_load(reinterpret_cast<const i32x2*>(mp));
+      mk[it][0] = i32x4{m2[0], m2[1], 0, 0};
+    }
+  }
+  // Indexer query: D int8 as D/4 packed dwords (uniform across the workgroup),
+  // and its bit-planes qp[t][w]: bit k of dword w is bit t of q[32w + k]
+  // (two's complement, so plane 7 weighs -128).  Every wave builds them with
+  // ballots, lane l holding q[l] (and q[64 + l] when D = 128).
   int32_t qw[D / 4];
   const int32_t* q32 = reinterpret_cast<const int32_t*>(q_index + (size_t)s * D);
 #pragma unroll
   for (int i = 0; i < D / 4; ++i) qw[i] = q32[i];
-
-  i32x4 v[kScoreIters][D / 8];
+  int32_t qsum = 0;
 #pragma unroll
-  for (int it = 0; it < kScoreIters; ++it) {
-    const int j = min(c * kScoreChunk + it * kScoreThreads + (int)threadIdx.x, nb - 1);
-    const int8_t* base = ckey + (size_t)page[it] * page_bytes + (size_t)(j & (bpp - 1)) * 16;
+  for (int i = 0; i < D / 4; ++i) qsum = __builtin_amdgcn_sdot4(qw[i], 0x01010101, qsum, false);
+  const int lane = threadIdx.x & 63;
+  uint32_t qp[8][kMaskWords];
 #pragma unroll
-    for (int ch = 0; ch < D / 8; ++ch)  // streamed once: non-temporal
-      v[it][ch] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(base + (size_t)ch * bpp * 16));
+  for (int h = 0; h < (D + 63) / 64; ++h) {
+    const int dim = 64 * h + lane;
+    const int qv = (int)q_index[(size_t)s * D + min(dim, D - 1)];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(dim < D && ((qv >> t) & 1));
+      qp[t][2 * h] = (uint32_t)m;
+      if (2 * h + 1 < kMaskWords) qp[t][2 * h + 1] = (uint32_t)(m >> 32);
+    }
   }
-  int32_t* srow = ws.scores + (size_t)s * ws.nb_stride;
+  for (int i = threadIdx.x; i < kBins; i += kScoreThreads) hist[i] = 0;
   int32_t sc[kScoreIters];
 #pragma unroll
   for (int it = 0; it < kScoreIters; ++it) {
-    int32_t lo = 0, hi = 0;
+    int32_t sd = 0;
 #pragma unroll
-    for (int ch = 0; ch < D / 16; ++ch) {
+    for (int ch = 0; ch < kSChunks; ++ch)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo = __builtin_amdgcn_sdot4(v[it][ch][e], qw[4 * ch + e], lo, false);
-        hi = __builtin_amdgcn_sdot4(v[it][ch + D / 16][e], qw[4 * ch + e], hi, false);
+      for (int e = 0; e < 4; ++e) sd = __builtin_amdgcn_sdot4(v[it][ch][e], qw[4 * ch + e], sd, false);
+    // hq = sum_i q[i] (2 b1[i] + b0[i]) = sum_t w_t (2 |Q_t & B1| + |Q_t & B0|)
+    int32_t hq = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint32_t p0 = 0, p1 = 0;
+#pragma unroll
+      for (int w = 0; w < kMaskWords; ++w) {
+        const int x0 = w, x1 = kMaskWords + w;   // mask dword index of b0, b1
+        p0 = __builtin_popcount(qp[t][w] & (uint32_t)mk[it][x0 >> 2][x0 & 3]) + p0;
+        p1 = __builtin_popcount(qp[t][w] & (uint32_t)mk[it][x1 >> 2][x1 & 3]) + p1;
       }
+      const int32_t xt = (int32_t)(2 * p1 + p0);
+      hq += (t == 7) ? -(xt << 7) : (xt << t);
     }
-    sc[it] = lo + hi * 256;
+    sc[it] = 256 * hq + sd - 384 * qsum;
   }
-  // No branches here either: the workspace has score slots up to the chunk's
-  // end (slots past the row's end are never read), and blocks past the end add
-  // 0 to the histogram.
+  __syncthreads();  // histogram cleared (no key load is outstanding by now)
 #pragma unroll
   for (int it = 0; it < kScoreIters; ++it) {
     const int j = c * kScoreChunk + it * kScoreThreads + threadIdx.x;
-    srow[j] = sc[it];
     atomicAdd(&hist[score_bin(sc[it])], j < nb ? 1u : 0u);
   }
   __syncthreads();
-  // Per-row histogram in the workspace: device-scope atomics, read by the
-  // next kernel after this one has finished (no fence needed here).
+  // No branches here either: the workspace has score slots up to the chunk's
+  // end (slots past the row's end are never read).  The per-row histogram is
+  // merged with device-scope atomics, read by the next kernel after this one
+  // has finished (no fence needed here).
+  int32_t* srow = ws.scores + (size_t)s * ws.nb_stride;
+#pragma unroll
+  for (int it = 0; it < kScoreIters; ++it) srow[c * kScoreChunk + it * kScoreThreads + threadIdx.x] = sc[it];
   uint32_t* ghist = ws.hist + (size_t)s * kBins;
   for (int i = threadIdx.x; i < kBins; i += kScoreThreads) {
     const uint32_t h = hist[i];

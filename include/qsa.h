@@ -45,12 +45,15 @@
  *                bytes with k_scale / v_scale fp32 [num_pages, page_size] (one
  *                scale per token per tensor).  Token t of request b is at page
  *                block_table[b][t / page_size], slot t % page_size.
- *   ckey cache   int8 [num_pages, 2*D/16, page_size/4, 16]: micro-block j of a
- *                request lives in page block_table[b][4j / page_size], slot
- *                j % (page_size/4).  Its exact integer key C (sum of 4 int8 keys,
- *                |C| <= 512) is stored losslessly in two int8 planes,
- *                C = 256*hi + lo with lo = (int8)C and hi in [-2, 2]; chunk c < D/16
- *                holds lo bytes of dims [16c, 16c+16), chunk D/16 + c the hi bytes.
+ *   ckey cache   int8 [num_pages, page_size/4 * (D + D/4)]: micro-block j of a request
+ *                lives in page block_table[b][4j / page_size], slot j % (page_size/4).
+ *                Its exact integer key C (sum of 4 int8 keys, |C| <= 512) is stored
+ *                losslessly in 10 bits per dimension: with v = C + 512,
+ *                s = (v mod 256) - 128 (int8) and b0, b1 = bits 8 and 9 of v,
+ *                C = 256*(2*b1 + b0) + s - 384.  Page layout: first the s plane as
+ *                D/16 runs of [page_size/4 slots][16 bytes] (run r holds dims
+ *                [16r, 16r+16) of every slot), then per slot D/4 mask bytes (b0 of
+ *                dims 0..D-1, then b1; dim i is bit i%8 of byte i/8).
  *                Size: qsa_ckey_cache_bytes().
  *   ring         int8 [num_reqs, 4, D]: the keys of each request's open micro-block
  *                (slot t % 4).  Only slots of the open block are ever read.

@@ -94,15 +94,20 @@ def check_out(got: np.ndarray, ref: np.ndarray, tol: float, what: str):
 
 
 def ckey_blocks_from_cache(wl, ckey: np.ndarray, b: int, nb: int) -> np.ndarray:
-    """Read the library's compressed-key storage back as int64 [nb, D] (documented layout)."""
+    """Read the library's compressed-key storage back as int64 [nb, D] (the layout
+    documented in include/qsa.h: s plane + two bit-masks, C = 256(2 b1 + b0) + s - 384)."""
     D, page = wl.shape.index_dim, wl.shape.page_size
     bpp = page // 4
-    cache = ckey.reshape(-1, 2 * D // 16, bpp, 16)
+    per_page = bpp * (D + D // 4)
+    cache = ckey.reshape(-1, per_page)
     bt = wl.block_table[b].cpu().numpy()
     j = np.arange(nb)
     pages = bt[j // bpp]
     slots = j % bpp
-    blk = cache[pages, :, slots, :]              # [nb, 2D/16, 16]
-    lo = blk[:, : D // 16, :].reshape(nb, D).astype(np.int64)
-    hi = blk[:, D // 16:, :].reshape(nb, D).astype(np.int64)
-    return hi * 256 + lo
+    rows = cache[pages]                                     # [nb, per_page]
+    splane = rows[:, : bpp * D].reshape(nb, D // 16, bpp, 16)
+    sv = splane[np.arange(nb), :, slots, :].reshape(nb, D).astype(np.int64)
+    masks = rows[:, bpp * D:].reshape(nb, bpp, D // 4)[np.arange(nb), slots].astype(np.uint8)
+    bits = np.unpackbits(masks, axis=1, bitorder="little").astype(np.int64)  # [nb, 2D]
+    b0, b1 = bits[:, :D], bits[:, D:]
+    return 256 * (2 * b1 + b0) + sv - 384

@@ -73,7 +73,7 @@ def test_compress_rejects_null_and_misaligned(lib):
     assert compress(lib, cfg(), ckey=ctypes.c_void_p(0x10004)) == 1
     assert compress(lib, cfg(), nreq=-1) == 1
     assert compress(lib, cfg(), nreq=0) == 0  # nothing to do, nothing enqueued
-    assert lib.qsa_ckey_cache_bytes(ctypes.byref(cfg()), 10) == 10 * 64 // 4 * 2 * 64
+    assert lib.qsa_ckey_cache_bytes(ctypes.byref(cfg()), 10) == 10 * 64 // 4 * (64 + 64 // 4)
     assert lib.qsa_ckey_cache_bytes(ctypes.byref(cfg(compress_ratio=2)), 10) == 0
 
 
