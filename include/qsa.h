@@ -127,8 +127,9 @@ qsa_status qsa_compress(const qsa_config* cfg, int32_t num_reqs, int32_t max_new
 /*
  * Workspace of qsa_index_topk for num_sel_rows rows of context <= max_seq_len.
  * Returns 0 on a bad argument.  Before its FIRST use a workspace must be
- * cleared with qsa_index_topk_workspace_init(); every qsa_index_topk call
- * leaves its counters cleared again, so later calls need no clearing.
+ * cleared with qsa_index_topk_workspace_init(); every qsa_index_topk call that
+ * selects (topk != NULL) leaves its counters cleared again, so later calls need
+ * no clearing.
  */
 size_t qsa_index_topk_workspace_size(const qsa_config* cfg, int32_t num_sel_rows,
                                      int32_t max_seq_len);
@@ -151,9 +152,12 @@ qsa_status qsa_index_topk_workspace_init(void* workspace, size_t ws_bytes, hipSt
  *                the grid and the workspace.  Rows longer than it are treated
  *                as max_seq_len long.
  *   topk == NULL: score only.  The exact int32 scores are left in the first
- *                num_sel_rows * nb_stride * 4 bytes of the workspace (row s,
- *                block j at [s * nb_stride + j], nb_stride = max_seq_len/4
- *                rounded up to a multiple of 1024) and nothing is selected.
+ *                num_sel_rows * nb_stride * 4 bytes of the workspace
+ *                (row s, block j at int32 index s * nb_stride + j, nb_stride =
+ *                max_seq_len/4 rounded up to a multiple of 1024).  Nothing is
+ *                selected, and the histogram counters stay set: the next call
+ *                with topk != NULL on this workspace needs
+ *                qsa_index_topk_workspace_init() first.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (index_dim), WORKSPACE, HIP.
  */
 qsa_status qsa_index_topk(const qsa_config* cfg, int32_t num_sel_rows, int32_t max_seq_len,

@@ -111,6 +111,43 @@ def test_compress_skips_dummy_requests():
     assert torch.equal(before, layer.ckey)
 
 
+# ------------------------------------------------------------------ scan alone
+
+@pytest.mark.parametrize("D,page", [(32, 16), (64, 64), (128, 256), (128, 16)])
+def test_scores_only_match_oracle_scores(D, page):
+    """qsa_index_topk(topk=NULL): every exact int32 score against the oracle's q.C_j,
+    across index widths, page sizes and ragged lengths (one row per length)."""
+    shape = QSAShape(16, 2, 128, D, 512, page)
+    lens = [3, 4, 257, 1023, 1024, 1027, 4096 + 64 * 5 + 7, 9001]
+    wl = make_workload(shape, lens, seed=40 + D + page, device=DEV, name=f"scan-D{D}-p{page}")
+    say(f"[gpu] scores-only D={D} page={page}")
+    layer = QSALayer(wl, 1, poison=True)
+    layer.prefill()
+    layer.compress()
+    api.qsa_index_topk(layer.cfg, wl.q_index, wl.sel_req, wl.sel_seq_len, wl.block_table, layer.ckey,
+                       None, layer.workspace, layer.max_seq_len)
+    torch.cuda.synchronize()
+    h = host_copy(wl)
+    nb_stride = -(-(layer.max_seq_len // 4) // 1024) * 1024
+    sc = layer.workspace.view(torch.int32)[: wl.num_sel * nb_stride].cpu().numpy().reshape(wl.num_sel, nb_stride)
+    for s_ in range(wl.num_sel):
+        b = int(h.sel_req[s_])
+        L = int(h.sel_seq_len[s_])
+        nb = L // 4
+        ref = O.score_blocks(h.q_index[s_], O.compress_keys(h.keys[h.key_off[b]:h.key_off[b] + L], L))
+        got = sc[s_, :nb].astype(np.int64)
+        assert np.array_equal(got, ref), f"row {s_} (L={L}): first diff at {np.nonzero(got != ref)[0][:5]}"
+
+
+@pytest.mark.parametrize("D,page,P", [(32, 16, 3), (128, 64, 2), (128, 256, 5), (64, 16, 8)])
+def test_index_dims_and_page_sizes(D, page, P):
+    """Selection and attention for every built index width and several page sizes."""
+    shape = QSAShape(16, 2, 128, D, 512, page)
+    wl = make_workload(shape, [4097, 2052, 30000, 511, 12345], seed=60 + D + page, device=DEV,
+                       name=f"dims-D{D}-p{page}")
+    check_layer(wl, run(wl, P=P))
+
+
 # ------------------------------------------------------------------ small configs
 
 @pytest.mark.parametrize("cfg,scale", [(1, 1.0), (2, 1 / 16), (3, 1 / 64), (4, 1 / 64), (5, 1 / 200)])
