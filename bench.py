@@ -104,6 +104,117 @@ def cpu_baseline(wl, seconds: float):
                                       f"float64, one thread, {el:.1f} s"}
 
 
+# ---- the oracle on all host cores: spawned workers (they import numpy and the
+# oracle only, never the GPU runtime) read the workload from shared memory.
+_POOL = {}
+
+
+def _pool_init(spec):
+    from multiprocessing import shared_memory
+
+    from threadpoolctl import threadpool_limits
+    _POOL["limits"] = threadpool_limits(1)
+    _POOL["shm"] = []
+    arrs = {}
+    for name, (shm_name, shape, dtype) in spec["arrays"].items():
+        shm = shared_memory.SharedMemory(name=shm_name)  # the parent owns and unlinks it
+        _POOL["shm"].append(shm)
+        arrs[name] = np.ndarray(shape, dtype=np.dtype(dtype), buffer=shm.buf)
+    _POOL["a"] = arrs
+    _POOL["meta"] = spec["meta"]
+
+
+def _pool_rows(job):
+    """Worker: oracle rows (selecting rows start, start+1, ... cyclically) until the deadline."""
+    from oracle import qsa_oracle as O
+    start, deadline = job
+    a, m = _POOL["a"], _POOL["meta"]
+    k, qps, S = m["k"], m["q_per_sel"], m["num_sel"]
+    done, s = 0, start % S
+    while time.time() < deadline:
+        b = int(a["sel_req"][s])
+        L = int(a["sel_seq_len"][s])
+        off = int(a["key_off"][b])
+        topk = np.full((S, k), -1, dtype=np.int32)
+        topk[s] = O.index_topk_row(a["q_index"][s], a["keys"][off:off + L], L, k)
+        O.decode_rows(q=a["q"], q_per_sel=qps, sel_req=a["sel_req"], sel_seq_len=a["sel_seq_len"],
+                      row_seq_len=a["row_seq_len"], topk=topk, block_table=a["block_table"],
+                      page_size=m["page_size"], k_cache=a["k_cache"], v_cache=a["v_cache"],
+                      kv_dtype=m["kv_dtype"], scale=m["scale"], num_splits=1,
+                      k_scale=a.get("k_scale"), v_scale=a.get("v_scale"), rows=range(s * qps, (s + 1) * qps))
+        done += qps
+        s = (s + 1) % S
+    return done
+
+
+def cpu_baseline_pool(wl, seconds: float, procs: int):
+    """The same oracle work as cpu_baseline, in `procs` single-threaded processes."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+
+    from tests.harness import host_copy
+    h = host_copy(wl)
+    arrays = {n: getattr(h, n) for n in ("keys", "key_off", "block_table", "k_cache", "v_cache", "k_scale",
+                                          "v_scale", "q", "q_index", "sel_req", "sel_seq_len", "row_seq_len")}
+    spec = {"arrays": {}, "meta": {"k": wl.shape.topk_blocks, "q_per_sel": wl.q_per_sel, "num_sel": wl.num_sel,
+                                    "page_size": wl.shape.page_size, "kv_dtype": wl.shape.kv_dtype,
+                                    "scale": wl.shape.softmax_scale}}
+    owned = []
+    try:
+        for n, arr in arrays.items():
+            if arr is None:
+                continue
+            arr = np.ascontiguousarray(arr)
+            shm = shared_memory.SharedMemory(create=True, size=max(arr.nbytes, 1))
+            owned.append(shm)
+            np.ndarray(arr.shape, dtype=arr.dtype, buffer=shm.buf)[...] = arr
+            spec["arrays"][n] = (shm.name, arr.shape, arr.dtype.str)
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(procs, initializer=_pool_init, initargs=(spec,)) as pool:
+            pool.map(_pool_rows, [(i, 0.0) for i in range(procs)])  # start-up and first touch, untimed
+            t0 = time.time()
+            counts = pool.map(_pool_rows, [(i, t0 + seconds) for i in range(procs)])
+            el = time.time() - t0
+    finally:
+        for shm in owned:
+            shm.close()
+            shm.unlink()
+    done = int(sum(counts))
+    return {"value": done / el, "unit": "query-rows/s", "cores": procs, "kind": "oracle",
+            "sample": f"{done} query rows of layer 0 ({wl.name}) in {procs} single-threaded processes, "
+                      f"{el:.1f} s; each row: compress + score + select over the full context, then "
+                      f"attention + merge, numpy int64/float64"}
+
+
+def stream_ceiling(stream, reps: int = 10):
+    """Read rate of a plain streaming kernel (libqsa_ceiling.so) over 1 GiB, HIP events."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_attention_qsa_amd", "libqsa_ceiling.so"))
+    lib.qsa_stream_granule.restype = ctypes.c_size_t
+    lib.qsa_stream_sink_bytes.restype = ctypes.c_size_t
+    lib.qsa_stream_read.restype = ctypes.c_int
+    lib.qsa_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    g = lib.qsa_stream_granule()
+    nbytes = max(1, (1 << 30) // g) * g
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(lib.qsa_stream_sink_bytes(), dtype=torch.uint8, device="cuda")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        assert lib.qsa_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), sp) == 0
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        lib.qsa_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), sp)
+    b.record(stream)
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    return {"kernel": "qsa_stream_ceiling (2048 workgroups x 256 threads, 8 x 16 B non-temporal loads in flight)",
+            "bytes": nbytes, "GBps": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
+
+
 def measured_traffic():
     """HBM bytes per scan launch from the committed rocprofv3 counter summary,
     or None when the kernel source has changed since the counters were taken."""
@@ -204,18 +315,23 @@ def main():
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps - 1)]
     t_wall = time.perf_counter()
     with torch.cuda.stream(stream):
         e0.record(stream)
-        for _ in range(args.steps):
+        for i in range(args.steps):
             if graph is not None:
                 graph.replay()
             else:
                 step()
+            if i < args.steps - 1:
+                evs[i].record(stream)
         e1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1) / args.steps
+    marks = [e0] + evs + [e1]
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
 
     # Dominant kernel: the compressed-key scan (qsa_index_topk with topk=None runs
     # only that kernel).  Its launches for all layers, back to back, are captured
@@ -259,6 +375,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": per_step[len(per_step) // 2],
+        "ms_per_step_min": per_step[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -277,9 +395,14 @@ def main():
                      "bytes_per_launch": scan_per_launch, "avg_launch_us": kern_ms * 1e3,
                      "launches_timed": n_launches},
     }
+    res["stream_ceiling"] = stream_ceiling(stream)
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl0, args.cpu_seconds)
+        procs = max(1, min(16, os.cpu_count() or 1))
+        print(f"[bench] cpu baseline (oracle), one core then {procs} processes ...", file=sys.stderr, flush=True)
+        one = cpu_baseline(wl0, args.cpu_seconds)
+        many = cpu_baseline_pool(wl0, args.cpu_seconds, procs) if procs > 1 else one
+        many["single_core"] = {"value": one["value"], "cores": 1, "sample": one["sample"]}
+        res["cpu_baseline"] = many
     print(json.dumps(res))
 
 
