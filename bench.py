@@ -243,6 +243,86 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
 
 
+PREFILL_DESCR = ("chunked prefill: B=4 requests, the last 512-token chunk of a 65,536-token prompt "
+                 "(2,048 query rows, each with its own causal length), H 16/2, d=128, top-512 blocks, D=64, "
+                 "64-token shuffled pages, bf16 K/V")
+
+
+def prefill_bench(args):
+    """Chunked-prefill step (compress the chunk, per-row selection with the int8-GEMM scan,
+    attention, merge) over `--layers` independent layers; one JSON line."""
+    import torch
+
+    from block_sparse_attention_qsa_amd import api
+    from block_sparse_attention_qsa_amd.pipeline import QSAPrefill
+    from block_sparse_attention_qsa_amd.workloads import SHAPE_MAIN, make_prefill_workload
+    P = args.splits or 4
+    nl = min(args.layers, 4)
+    layers = []
+    for li in range(nl):
+        wl = make_prefill_workload(SHAPE_MAIN, [65536] * 4, 512, seed=7000 + li, device="cuda",
+                                   name="prefill-64k-chunk512")
+        layer = QSAPrefill(wl, num_splits=P)
+        layer.prefill()
+        layers.append(layer)
+        print(f"[bench] prefill layer {li} ready (rows={wl.num_rows})", file=sys.stderr, flush=True)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def timed(fn, reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            for layer in layers:
+                layer.step(stream)
+    torch.cuda.synchronize()
+    ms = timed(lambda: [layer.step(stream) for layer in layers], args.steps)
+    # the per-row selection alone (compress, then the GEMM scan + filter + finalize)
+    ms_index = timed(lambda: [(layer.compress(stream), layer.index(stream)) for layer in layers], args.steps)
+    # the scan kernel alone (scores only); it leaves the histograms set, so it runs last
+    def scan_only():
+        for layer in layers:
+            wl = layer.wl
+            api.qsa_prefill_index_topk(layer.cfg, wl.q_index, layer.row_cu, wl.row_seq_len, wl.block_table,
+                                       layer.ckey, None, layer.workspace, layer.max_seq_len, layer.max_rows,
+                                       stream=stream)
+    ms_scan = timed(scan_only, args.steps)
+    wl0 = layers[0].wl
+    lens = wl0.row_seq_len.cpu().numpy().astype(np.int64)
+    D = wl0.shape.index_dim
+    ops = 2.0 * float((lens // 4).sum()) * D                      # int8 multiply-adds of the scan, x2
+    scan_bytes = float(4 * (65536 // 4) * (D + D // 4) + wl0.num_rows * D)
+    rows = sum(l.wl.num_rows for l in layers)
+    per_launch_s = ms_scan * 1e-3 / nl
+    res = {"metric": "QSA chunked-prefill query-rows/s (per-row top-k + attention)",
+           "value": rows / (ms * 1e-3), "unit": "query-rows/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": PREFILL_DESCR, "layers_per_step": nl, "query_rows_per_layer": wl0.num_rows,
+                      "splits": P, "hip_graph": True},
+           "selection_ms_per_step": ms_index, "scan_us_per_launch": per_launch_s * 1e6,
+           "roofline": {"kernel": "qsa::prefill_score_kernel (int8 MFMA scan, 16 rows x 16 blocks per instruction)",
+                        "bound": "mfma", "achieved": ops / per_launch_s / 1e12, "peak": 5000.0,
+                        "unit": "TOP/s", "frac": ops / per_launch_s / 1e12 / 5000.0, "traffic": None,
+                        "ops_per_launch": ops, "compressed_key_bytes_per_launch": scan_bytes,
+                        "hbm_GBps_of_those_bytes": scan_bytes / per_launch_s / 1e9}}
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,6 +336,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    ap.add_argument("--prefill", action="store_true",
+                    help="measure the chunked-prefill path instead (its own JSON line)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -272,6 +354,9 @@ def main():
         build.build()
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
+        return
+    if args.prefill:
+        prefill_bench(args)
         return
     from block_sparse_attention_qsa_amd import api
     from block_sparse_attention_qsa_amd.pipeline import QSALayer

@@ -121,6 +121,25 @@ def qsa_index_topk(cfg: QSAConfig, q_index: torch.Tensor, sel_req: torch.Tensor,
                                       workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def qsa_prefill_index_topk(cfg: QSAConfig, q_index: torch.Tensor, row_cu: torch.Tensor,
+                           row_seq_len: torch.Tensor, block_table: torch.Tensor, ckey_cache: torch.Tensor,
+                           topk: torch.Tensor, workspace: torch.Tensor, max_seq_len: int,
+                           max_rows_per_req: int, stream=None) -> None:
+    """Top-k per prefill query row (rows of request b: [row_cu[b], row_cu[b+1])), the scan as an
+    int8 MFMA GEMM.  topk int32 [R, k] like qsa_index_topk; topk=None scores only."""
+    _dt(q_index, torch.int8); _dt(ckey_cache, torch.int8)
+    if topk is not None:
+        _dt(topk, torch.int32)
+    _dt(row_cu, torch.int32); _dt(row_seq_len, torch.int32); _dt(block_table, torch.int32)
+    c = cfg.to_c()
+    B = row_cu.shape[0] - 1
+    R = row_seq_len.shape[0]
+    _check(_lib.load().qsa_prefill_index_topk(ctypes.byref(c), B, R, int(max_rows_per_req), int(max_seq_len),
+                                              _ptr(q_index), _ptr(row_cu), _ptr(row_seq_len), _ptr(block_table),
+                                              _ptr(ckey_cache), _ptr(topk), _ptr(workspace),
+                                              workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 def qsa_sparse_decode(cfg: QSAConfig, q: torch.Tensor, row_seq_len: torch.Tensor,
                       sel_req: torch.Tensor, sel_seq_len: torch.Tensor, topk: torch.Tensor,
                       block_table: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

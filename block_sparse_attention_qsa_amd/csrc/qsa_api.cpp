@@ -135,6 +135,36 @@ qsa_status qsa_index_topk(const qsa_config* cfg, int32_t num_sel_rows, int32_t m
                            block_table, ckey_cache, topk, lay, workspace, stream);
 }
 
+qsa_status qsa_prefill_index_topk(const qsa_config* cfg, int32_t num_reqs, int32_t num_rows,
+                                  int32_t max_rows_per_req, int32_t max_seq_len,
+                                  const int8_t* q_index, const int32_t* row_cu,
+                                  const int32_t* row_seq_len, const int32_t* block_table,
+                                  const int8_t* ckey_cache, int32_t* topk,
+                                  void* workspace, size_t ws_bytes, hipStream_t stream) {
+  qsa_status st = check_config(cfg, true, false);
+  if (st != QSA_OK) return st;
+  if (num_reqs < 0 || num_reqs > 65535)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "num_reqs must be in [0, 65535] (got %d)", num_reqs);
+  if (num_rows < 0 || num_rows > 65535)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "num_rows must be in [0, 65535] (got %d)", num_rows);
+  if (max_rows_per_req < 0 || max_rows_per_req > num_rows)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "max_rows_per_req must be in [0, num_rows] (got %d)", max_rows_per_req);
+  if (max_seq_len < 0 || max_seq_len > QSA_MAX_SEQ_LEN)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "max_seq_len must be in [0, %d] (got %d)", QSA_MAX_SEQ_LEN, max_seq_len);
+  if (num_rows == 0 || num_reqs == 0) return QSA_OK;
+  if (!q_index || !row_cu || !row_seq_len || !block_table || !ckey_cache)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_prefill_index_topk: NULL array argument");
+  if (!aligned(ckey_cache, 16) || !aligned(q_index, 16))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_prefill_index_topk: ckey_cache and q_index need 16-byte alignment");
+  TopkWorkspace lay = topk_workspace_layout(num_rows, max_seq_len);
+  if (!workspace) return fail(QSA_ERR_WORKSPACE, "qsa_prefill_index_topk: workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(QSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < lay.total)
+    return fail(QSA_ERR_WORKSPACE, "qsa_prefill_index_topk: workspace has %zu bytes, needs %zu", ws_bytes, lay.total);
+  return launch_prefill_index_topk(*cfg, num_reqs, num_rows, max_rows_per_req, max_seq_len, q_index, row_cu,
+                                   row_seq_len, block_table, ckey_cache, topk, lay, workspace, stream);
+}
+
 qsa_status qsa_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_t q_per_sel,
                              int32_t num_splits, const void* q, const int32_t* row_seq_len,
                              const int32_t* sel_req, const int32_t* sel_seq_len,

@@ -438,6 +438,147 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   for (int i = (int)ks + tid; i < k; i += kFinThreads) out[i] = -1;
 }
 
+// ---------------------------------------------------------------------------
+// Prefill scoring (many query rows per request, each with its own causal
+// length): the scan becomes an int8 GEMM, rows x blocks.  A workgroup takes 16
+// rows of one request (the MFMA M dimension) and a chunk of 1,024 blocks; each
+// of its 4 waves takes 16 tiles of 16 blocks.  Per tile,
+//   v_mfma_i32_16x16x64_i8(q, s)  and  v_mfma_i32_16x16x64_i8(q, h),
+// h = 2 b1 + b0 expanded from the bit-masks to bytes, give
+// score = q.s + 256 q.h - 384 sum(q) exactly in int32.  The B operand of lane l
+// is the 16-byte s-plane chunk l/16 of block l%16: a plain 16-byte load from
+// the page, no LDS.  Per-row histograms (16-bit counts, two per LDS word) are
+// merged into the rows' histograms as in the decode scan; the filter and
+// finalize kernels then select exactly as for qsa_index_topk.
+constexpr int kPfThreads = 256;
+constexpr int kPfRows = 16;
+constexpr int kPfTiles = kScoreChunk / (kPfThreads / 64) / 16;  // block tiles per wave
+
+__device__ __forceinline__ uint32_t spread_nibble(uint32_t n) {  // bit e of n -> byte e (0/1)
+  return (n * 0x00204081u) & 0x01010101u;
+}
+
+__device__ __forceinline__ int32_t sum_lane_groups(int32_t v) {  // sum over lanes l, l^16, l^32, l^48
+  auto a = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = (int32_t)(a[0] + a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return (int32_t)(b[0] + b[1]);
+}
+
+template <int D>
+__global__ __launch_bounds__(kPfThreads) void prefill_score_kernel(
+    const int8_t* __restrict__ q_index, const int32_t* __restrict__ row_cu,
+    const int32_t* __restrict__ row_seq_len, const int32_t* __restrict__ block_table,
+    int32_t max_pages, int32_t page_log2, const int8_t* ckey, int32_t max_seq_len, WsPtrs ws) {
+  constexpr int KS = (D + 63) / 64;  // MFMA k-steps of 64 dims (D = 32: the upper half is zero)
+  constexpr int kSChunks = D / 16;
+  __shared__ uint32_t hist[kPfRows * kBins / 2];
+  const int c = blockIdx.x, tile = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int r_end = row_cu[b + 1];
+  const int r0 = row_cu[b] + tile * kPfRows;
+  if (r0 >= r_end) return;
+  // Lane col holds row r0+col: its length (0 past the request's rows).
+  const int rc = min(r0 + col, r_end - 1);
+  const int lr = (r0 + col < r_end) ? min(row_seq_len[rc], max_seq_len) : 0;
+  const int nbc = max(lr, 0) >> 2;
+  int nbmax = nbc;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) nbmax = max(nbmax, __shfl_xor(nbmax, o, 64));
+  if (c * kScoreChunk >= nbmax) return;  // uniform: every row of the tile ends before this chunk
+  const int bpp_log2 = page_log2 - 2;
+  const int bpp = 1 << bpp_log2;
+  const size_t page_bytes = (size_t)bpp * (D + D / 4);
+  const int32_t* bt = block_table + (size_t)b * max_pages;
+
+  // A operand: row r0+col, dims 64 ks + 16 g .. +15 (zero past the request's rows or past D).
+  i32x4 qa[KS];
+  int32_t qpart = 0;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int dim = 64 * ks + 16 * g;
+    const i32x4 v = *reinterpret_cast<const i32x4*>(q_index + (size_t)rc * D + min(dim, D - 16));
+    const bool live = (r0 + col < r_end) && dim < D;
+    qa[ks] = live ? v : i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qpart = __builtin_amdgcn_sdot4(qa[ks][e], 0x01010101, qpart, false);
+  }
+  const int32_t qsum_col = sum_lane_groups(qpart);  // sum(q) of row r0+col
+  int32_t qsum_m[4], nb_m[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // C rows 4g+i of this lane
+    qsum_m[i] = __shfl(qsum_col, 4 * g + i, 64);
+    nb_m[i] = __shfl(nbc, 4 * g + i, 64);
+  }
+
+  // Page ids of the wave's tiles, then all key loads (blocks clamped to the
+  // tile's longest row: they exist in the cache).
+  const int jw = c * kScoreChunk + w * (kPfTiles * 16);
+  int pg[kPfTiles];
+#pragma unroll
+  for (int t = 0; t < kPfTiles; ++t) {
+    const int jc = min(jw + 16 * t + col, nbmax - 1);
+    pg[t] = bt[jc >> bpp_log2];
+  }
+  i32x4 bs[kPfTiles][KS];
+  uint32_t m0[kPfTiles][KS], m1[kPfTiles][KS];
+#pragma unroll
+  for (int t = 0; t < kPfTiles; ++t) {
+    const int jc = min(jw + 16 * t + col, nbmax - 1);
+    const int slot = jc & (bpp - 1);
+    const int8_t* page = ckey + (size_t)pg[t] * page_bytes;
+    const uint8_t* mp = reinterpret_cast<const uint8_t*>(page + (size_t)kSChunks * bpp * 16 + (size_t)slot * (D / 4));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch = min(4 * ks + g, kSChunks - 1);
+      bs[t][ks] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(page + (size_t)ch * bpp * 16 + (size_t)slot * 16));
+      m0[t][ks] = *reinterpret_cast<const uint16_t*>(mp + 2 * ch);
+      m1[t][ks] = *reinterpret_cast<const uint16_t*>(mp + D / 8 + 2 * ch);
+    }
+  }
+  for (int i = threadIdx.x; i < kPfRows * kBins / 2; i += kPfThreads) hist[i] = 0;
+  __syncthreads();
+
+#pragma unroll
+  for (int t = 0; t < kPfTiles; ++t) {
+    i32x4 cs = {0, 0, 0, 0}, chh = {0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bool live = 64 * ks + 16 * g < D;
+      i32x4 bh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        bh[e] = (int32_t)(spread_nibble((m0[t][ks] >> (4 * e)) & 15u) + 2u * spread_nibble((m1[t][ks] >> (4 * e)) & 15u));
+      const i32x4 bsv = live ? bs[t][ks] : i32x4{0, 0, 0, 0};
+      bh = live ? bh : i32x4{0, 0, 0, 0};
+      cs = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[ks], bsv, cs, 0, 0, 0);
+      chh = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[ks], bh, chh, 0, 0, 0);
+    }
+    const int j = jw + 16 * t + col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * g + i;
+      const int r = r0 + m;
+      const int32_t sc = cs[i] + 256 * chh[i] - 384 * qsum_m[i];
+      const bool valid = j < nb_m[i];  // rows past the request's end have nb 0
+      const int bin = score_bin(sc);
+      atomicAdd(&hist[(m * kBins + bin) >> 1], valid ? ((bin & 1) ? 0x10000u : 1u) : 0u);
+      if (r < r_end) ws.scores[(size_t)r * ws.nb_stride + j] = sc;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kPfRows * kBins / 2; i += kPfThreads) {
+    const uint32_t h = hist[i];
+    const int m = (2 * i) / kBins, bin = (2 * i) % kBins;
+    if (h && r0 + m < r_end) {
+      uint32_t* gh = ws.hist + (size_t)(r0 + m) * kBins + bin;
+      if (h & 0xffffu) atomicAdd(gh, h & 0xffffu);
+      if (h >> 16) atomicAdd(gh + 1, h >> 16);
+    }
+  }
+}
+
 __global__ void clear_kernel(uint32_t* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0;
@@ -518,6 +659,52 @@ qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len
   hipLaunchKernelGGL(finalize_kernel, dim3(S), dim3(kFinThreads), 0, stream, sel_seq_len, c.topk_blocks,
                      max_seq_len, topk, ws);
   return check_launch("qsa_index_topk(finalize)");
+}
+
+qsa_status launch_prefill_index_topk(const qsa_config& c, int32_t B, int32_t R, int32_t max_rows,
+                                     int32_t max_seq_len, const int8_t* q_index, const int32_t* row_cu,
+                                     const int32_t* row_seq_len, const int32_t* block_table,
+                                     const int8_t* ckey, int32_t* topk, const TopkWorkspace& lay,
+                                     void* ws_base, hipStream_t stream) {
+  if (R == 0 || B == 0) return QSA_OK;
+  char* base = reinterpret_cast<char*>(ws_base);
+  WsPtrs ws;
+  ws.scores = reinterpret_cast<int32_t*>(base + lay.off_scores);
+  ws.keys = reinterpret_cast<uint64_t*>(base + lay.off_keys);
+  ws.bitmap = reinterpret_cast<uint64_t*>(base + lay.off_bitmap);
+  ws.keys2 = reinterpret_cast<uint64_t*>(base + lay.off_keys2);
+  ws.hist = reinterpret_cast<uint32_t*>(base + lay.off_hist);
+  ws.ccount = reinterpret_cast<uint32_t*>(base + lay.off_ccount);
+  ws.meta = reinterpret_cast<int32_t*>(base + lay.off_meta);
+  ws.nb_stride = lay.nb_stride;
+  const int page_log2 = __builtin_ctz((unsigned)c.page_size);
+  const int chunks = lay.nb_stride / kScoreChunk;
+  dim3 grid(chunks, (max_rows + kPfRows - 1) / kPfRows, B);
+  switch (c.index_dim) {
+    case 32:
+      hipLaunchKernelGGL(prefill_score_kernel<32>, grid, dim3(kPfThreads), 0, stream, q_index, row_cu,
+                         row_seq_len, block_table, c.max_pages_per_req, page_log2, ckey, max_seq_len, ws);
+      break;
+    case 64:
+      hipLaunchKernelGGL(prefill_score_kernel<64>, grid, dim3(kPfThreads), 0, stream, q_index, row_cu,
+                         row_seq_len, block_table, c.max_pages_per_req, page_log2, ckey, max_seq_len, ws);
+      break;
+    case 128:
+      hipLaunchKernelGGL(prefill_score_kernel<128>, grid, dim3(kPfThreads), 0, stream, q_index, row_cu,
+                         row_seq_len, block_table, c.max_pages_per_req, page_log2, ckey, max_seq_len, ws);
+      break;
+    default:
+      return fail(QSA_ERR_UNSUPPORTED, "index_dim %d not built", c.index_dim);
+  }
+  qsa_status st = check_launch("qsa_prefill_index_topk(score)");
+  if (st != QSA_OK || topk == nullptr) return st;
+  hipLaunchKernelGGL(filter_kernel, dim3(chunks, R), dim3(kThreads), 0, stream, row_seq_len, c.topk_blocks,
+                     max_seq_len, ws);
+  st = check_launch("qsa_prefill_index_topk(filter)");
+  if (st != QSA_OK) return st;
+  hipLaunchKernelGGL(finalize_kernel, dim3(R), dim3(kFinThreads), 0, stream, row_seq_len, c.topk_blocks,
+                     max_seq_len, topk, ws);
+  return check_launch("qsa_prefill_index_topk(finalize)");
 }
 
 }  // namespace qsa

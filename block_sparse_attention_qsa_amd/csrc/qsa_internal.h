@@ -46,6 +46,12 @@ qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len
                              const int8_t* ckey, int32_t* topk, const TopkWorkspace& ws,
                              void* ws_base, hipStream_t stream);
 
+qsa_status launch_prefill_index_topk(const qsa_config& c, int32_t B, int32_t R, int32_t max_rows,
+                                     int32_t max_seq_len, const int8_t* q_index, const int32_t* row_cu,
+                                     const int32_t* row_seq_len, const int32_t* block_table,
+                                     const int8_t* ckey, int32_t* topk, const TopkWorkspace& ws,
+                                     void* ws_base, hipStream_t stream);
+
 qsa_status launch_ws_clear(void* ws, size_t bytes, hipStream_t stream);
 
 qsa_status launch_sparse_decode(const qsa_config& c, int32_t S, int32_t q_per_sel, int32_t P,

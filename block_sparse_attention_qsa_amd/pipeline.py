@@ -110,3 +110,21 @@ class QSALayer:
         self.index(stream)
         self.decode(stream)
         self.merge(stream)
+
+
+class QSAPrefill(QSALayer):
+    """Chunked prefill (a workload from make_prefill_workload): compress the chunk,
+    select per query row with qsa_prefill_index_topk (the scan as an int8 GEMM),
+    attend with qsa_sparse_decode (one selecting row per query row), merge."""
+
+    def __init__(self, wl: Workload, num_splits: int = 1, poison: bool = False,
+                 max_seq_len: Optional[int] = None, out_dtype: torch.dtype = torch.float32):
+        super().__init__(wl, num_splits=num_splits, poison=poison, max_seq_len=max_seq_len, out_dtype=out_dtype)
+        self.row_cu = wl.extra["row_cu"]
+        self.max_rows = int(wl.extra["max_rows_per_req"])
+
+    def index(self, stream=None) -> None:
+        wl = self.wl
+        api.qsa_prefill_index_topk(self.cfg, wl.q_index, self.row_cu, wl.row_seq_len, wl.block_table, self.ckey,
+                                   self.topk, self.workspace, self.max_seq_len, self.max_rows, stream=stream)
+

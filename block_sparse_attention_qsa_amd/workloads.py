@@ -172,6 +172,39 @@ def make_workload(shape: QSAShape, final_len: List[int], *, step_tokens: int = 1
         row_seq_len=torch.as_tensor(row_len.astype(np.int32), device=device), q=q)
 
 
+def make_prefill_workload(shape: QSAShape, final_len: List[int], chunk, *, seed: int = 0,
+                          device: str = "cpu", name: str = "prefill", shuffle_pages: bool = True) -> Workload:
+    """Chunked prefill: request b appends its last chunk[b] tokens (an int applies to
+    all), and every appended token is a query row with its own selection: row t of
+    request b has context prefix_b + 1 + t (causal).  S = R = sum(chunk);
+    sel_req[r] is the row's request; extra["row_cu"] (int32 [B+1]) delimits the
+    requests' rows; the K/V and compressed caches hold every token up to final_len."""
+    fl = np.asarray(final_len, dtype=np.int64)
+    B = fl.shape[0]
+    ch = np.broadcast_to(np.asarray(chunk, dtype=np.int64), (B,)).copy()
+    base = make_workload(shape, list(fl), step_tokens=int(ch.max()), q_per_sel=1, seed=seed, device=device,
+                         name=name, shuffle_pages=shuffle_pages)
+    prefix = np.maximum(fl - ch, 0)
+    rows = np.concatenate([prefix[b] + 1 + np.arange(fl[b] - prefix[b]) for b in range(B)]).astype(np.int64)
+    counts = fl - prefix
+    row_cu = np.zeros(B + 1, dtype=np.int64)
+    row_cu[1:] = np.cumsum(counts)
+    R = int(row_cu[-1])
+    g = _gen(seed + 7919, device)
+    sel_req = np.repeat(np.arange(B), counts)
+    q_index = torch.randint(-127, 128, (R, shape.index_dim), generator=g, device=device, dtype=torch.int8)
+    q = torch.randn((R, shape.num_q_heads, shape.head_dim), generator=g, device=device).to(torch.bfloat16)
+    lens = torch.as_tensor(rows.astype(np.int32), device=device)
+    return Workload(
+        name=name, shape=shape, seed=seed, device=device, final_len=fl, prefix_len=prefix,
+        keys=base.keys, key_off=base.key_off, block_table=base.block_table, num_pages=base.num_pages,
+        k_cache=base.k_cache, v_cache=base.v_cache, k_scale=base.k_scale, v_scale=base.v_scale,
+        q_per_sel=1, sel_req=torch.as_tensor(sel_req.astype(np.int32), device=device),
+        sel_seq_len=lens, q_index=q_index, row_seq_len=lens.clone(), q=q,
+        extra={"row_cu": torch.as_tensor(row_cu.astype(np.int32), device=device),
+               "max_rows_per_req": int(counts.max()) if B else 0})
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads
 # ---------------------------------------------------------------------------

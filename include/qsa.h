@@ -167,6 +167,34 @@ qsa_status qsa_index_topk(const qsa_config* cfg, int32_t num_sel_rows, int32_t m
                           void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * qsa_prefill_index_topk -- qsa_index_topk for a chunk of prefill query rows:
+ * many rows per request, each with its own causal length (sparse / chunked
+ * prefill; [QSA-DCP], section on why the pull request matters, names a native
+ * sparse-prefill kernel for the QSA path as companion work).  [QSA-DCP]: the
+ * indexer keeps the best 512 compressed blocks per query; [PR53896]:
+ * weight-free top-k, fixed-width int32 output padded with -1.
+ *
+ * Rows r in [row_cu[b], row_cu[b+1]) belong to request b (row_cu int32 [B+1],
+ * row_cu[0] = 0, row_cu[B] = num_rows, at most max_rows_per_req rows per
+ * request); row r has context L = row_seq_len[r].  topk[r] is exactly what
+ * qsa_index_topk gives for a selecting row with sel_req = b and sel_seq_len =
+ * row_seq_len[r].  The scan is a GEMM (int8 MFMA, 16 rows x 16 blocks per
+ * instruction): each compressed block is read once per 16 rows instead of once
+ * per row.
+ *   q_index int8 [num_rows, D] (16-byte aligned); workspace: from
+ *   qsa_index_topk_workspace_size(cfg, num_rows, max_seq_len), initialised
+ *   once; topk == NULL leaves the scores (layout as for qsa_index_topk) and
+ *   histogram counters set.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (index_dim), WORKSPACE, HIP.
+ */
+qsa_status qsa_prefill_index_topk(const qsa_config* cfg, int32_t num_reqs, int32_t num_rows,
+                                  int32_t max_rows_per_req, int32_t max_seq_len,
+                                  const int8_t* q_index, const int32_t* row_cu,
+                                  const int32_t* row_seq_len, const int32_t* block_table,
+                                  const int8_t* ckey_cache, int32_t* topk,
+                                  void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * qsa_sparse_decode -- attention of the query rows over the selected tokens,
  * as num_splits partial results.  [QSA-DCP]: softmax and value aggregation over
  * the uncompressed K/V at the kept positions; each context-parallel partition

@@ -111,3 +111,27 @@ def ckey_blocks_from_cache(wl, ckey: np.ndarray, b: int, nb: int) -> np.ndarray:
     bits = np.unpackbits(masks, axis=1, bitorder="little").astype(np.int64)  # [nb, 2D]
     b0, b1 = bits[:, :D], bits[:, D:]
     return 256 * (2 * b1 + b0) + sv - 384
+
+
+def check_layer(wl, layer, h=None, rows=None, topk_ref=None):
+    h = h or host_copy(wl)
+    tol = OUT_TOL[wl.shape.kv_dtype]
+    sel_rows = None if rows is None else sorted({r // wl.q_per_sel for r in rows})
+    ref_topk = oracle_topk(wl, h, sel_rows) if topk_ref is None else topk_ref
+    got_topk = layer.topk.cpu().numpy()
+    srows = range(wl.num_sel) if sel_rows is None else sel_rows
+    for s in srows:
+        assert np.array_equal(got_topk[s], ref_topk[s]), \
+            f"{wl.name}: topk mismatch row {s}: first diff at {np.nonzero(got_topk[s] != ref_topk[s])[0][:5]}"
+    ref = oracle_decode(wl, h, ref_topk, layer.P, rows=rows)
+    rr = list(range(wl.num_rows)) if rows is None else list(rows)
+    o_part = layer.o_part.cpu().numpy()[:, rr]
+    lse_part = layer.lse_part.cpu().numpy()[:, rr]
+    out = layer.out.float().cpu().numpy()[rr]
+    lse = layer.lse.cpu().numpy()[rr]
+    e1 = check_out(o_part, ref["o_part"], tol, f"{wl.name} o_part")
+    check_lse(lse_part, ref["lse_part"], f"{wl.name} lse_part")
+    e2 = check_out(out, ref["out"], tol, f"{wl.name} out")
+    check_lse(lse, ref["lse"], f"{wl.name} lse")
+    say(f"[gpu] {wl.name} ok: max|d o_part|={e1:.2e} max|d out|={e2:.2e}")
+    return ref

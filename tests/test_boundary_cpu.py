@@ -98,6 +98,30 @@ def test_workspace_size_and_checks(lib):
     assert lib.qsa_index_topk_workspace_init(None, 100, None) == 3
 
 
+def test_prefill_index_topk_rejects(lib):
+    c = cfg()
+    n = lib.qsa_index_topk_workspace_size(ctypes.byref(c), 64, 65536)
+
+    def pf(ws=FAKE, nbytes=n, B=2, R=64, M=32, L=65536, q=FAKE, cu=FAKE, **kw):
+        return lib.qsa_prefill_index_topk(ctypes.byref(kw.get("c", c)), B, R, M, L, q, cu, FAKE, FAKE, FAKE,
+                                          FAKE, ws, nbytes, None)
+    assert pf(nbytes=n - 1) == 3
+    assert pf(ws=None) == 3
+    assert pf(ws=ctypes.c_void_p(0x10010)) == 3
+    assert pf(L=_lib.QSA_MAX_SEQ_LEN + 4) == 1
+    assert pf(B=-1) == 1
+    assert pf(R=-1) == 1
+    assert pf(R=70000) == 1
+    assert pf(M=65) == 1                            # more rows per request than rows
+    assert pf(q=None) == 1
+    assert pf(cu=None) == 1
+    assert pf(q=ctypes.c_void_p(0x10004)) == 1       # q_index not 16-byte aligned
+    assert pf(c=cfg(index_dim=96)) == 2
+    assert pf(c=cfg(compress_ratio=2)) == 1
+    assert pf(R=0, M=0) == 0
+    assert pf(B=0) == 0
+
+
 def decode(lib, c, P=2, qps=1, S=4, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, o=FAKE, l=FAKE)
     a.update(kw)
