@@ -7,25 +7,27 @@
 // int32 buffer padded with -1.  Ties go to the lower block index, so the
 // result is unique and can be compared bit for bit.
 //
-// Three kernels, no fences and no inter-workgroup waits (each kernel boundary
-// publishes the previous kernel's results):
+// Two kernels, no fences and no inter-workgroup waits (the kernel boundary
+// publishes the scan's results):
 //   score    (grid: chunk of 1024 micro-blocks x selecting row): streams the
 //            10-bit compressed keys (the HBM-bound scan: an int8 plane s and two
 //            bit-masks b0, b1 per block), computes
 //            score = q.s (v_dot4_i32_i8) + 256 (2 q.b1 + q.b0) - 384 sum(q),
 //            the masked sums as popcounts of the masks against the query's
-//            bit-planes (built per wave with ballots), stores
-//            the int32 score and adds an LDS histogram of the score's top 11
-//            bits into a per-row histogram with device-scope atomics.
-//   filter   (same grid): each workgroup derives the threshold bin T from the
-//            row histogram (fewer than k scores above T, at least k at or above
-//            it), writes bitmap words of its blocks above T and appends 64-bit
-//            keys (score, ~index) of its blocks inside T to the row's list.
-//   finalize (one workgroup per selecting row): radix-selects the missing
-//            blocks among the candidates (usually a few hundred), sets their
-//            bits, emits the bitmap in ascending order with a popcount prefix
-//            sum and pads with -1.  It clears the row's histogram and candidate
-//            count, so the workspace stays clean between calls.
+//            bit-planes (built per wave with ballots), stores the int32 score,
+//            adds an LDS histogram of the score's top 11 bits into the row's
+//            histogram with device-scope atomics, and from that LDS histogram
+//            writes the chunk's candidate list (every block at or above the
+//            bin of its m-th best block; see chunk_candidates).
+//   finalize (one workgroup per selecting row): the row's threshold bin T
+//            (fewer than k scores above T, at least k at or above it) from the
+//            row histogram; the chunks' lists, loaded in one round, are
+//            classified against T (a chunk whose list may be short is re-read
+//            from its scores); the missing blocks among the bin-T candidates
+//            (usually a few hundred) are picked by a radix select; the bitmap
+//            is emitted in ascending order with a popcount prefix sum and
+//            padded with -1.  It clears the row's histogram, so the workspace
+//            stays clean between calls.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -33,10 +35,10 @@ namespace qsa {
 
 namespace {
 
-constexpr int kThreads = 256;                          // filter kernel
-constexpr int kIters = kScoreChunk / kThreads;
 constexpr int kScoreThreads = 512;                     // score kernel
 constexpr int kScoreIters = kScoreChunk / kScoreThreads;
+constexpr int kCandThreads = 256;                      // chunk-candidate kernel (prefill)
+constexpr int kCandIters = kScoreChunk / kCandThreads;
 
 struct WsPtrs {
   int32_t* scores;
@@ -44,8 +46,7 @@ struct WsPtrs {
   uint64_t* bitmap;
   uint64_t* keys2;
   uint32_t* hist;
-  uint32_t* ccount;
-  int32_t* meta;
+  uint32_t* cinfo;
   int32_t nb_stride;
 };
 
@@ -55,6 +56,101 @@ __device__ __forceinline__ int score_bin(int32_t s) {
 
 __device__ __forceinline__ uint64_t cand_key(int32_t score, uint32_t j) {
   return ((uint64_t)((uint32_t)score ^ 0x80000000u) << 32) | (uint64_t)(0xffffffffu - j);
+}
+
+__device__ __forceinline__ int32_t key_score(uint64_t key) {
+  return (int32_t)((uint32_t)(key >> 32) ^ 0x80000000u);
+}
+
+// Block-wide exclusive prefix sum (blockDim.x threads, a multiple of 64).
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh /*[NT/64]*/) {
+  const int l = lane_id(), w = threadIdx.x / 64;
+  const uint32_t inc = wave_incl_scan(v);
+  if (l == 63) sh[w] = inc;
+  __syncthreads();
+  uint32_t off = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) off += (i < w) ? sh[i] : 0u;
+  __syncthreads();
+  return off + inc - v;
+}
+
+// Threshold bin from a histogram held as per-thread counts (thread t holds
+// bins kBins-1-(kPer t + i), i.e. descending): the bin T with
+// count(bins > T) < ks <= count(bins >= T).  Writes (T, count above T).
+template <int NT>
+__device__ __forceinline__ void threshold_from_counts(const uint32_t (&cnt)[kBins / NT], uint32_t ks,
+                                                      uint32_t* sh, int32_t* s_T, uint32_t* s_above) {
+  constexpr int kPer = kBins / NT;
+  const int tid = threadIdx.x;
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) mine += cnt[i];
+  uint32_t above = block_excl_scan<NT>(mine, sh);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (above < ks && above + cnt[i] >= ks) { *s_T = kBins - 1 - (kPer * tid + i); *s_above = above; }
+    above += cnt[i];
+  }
+  __syncthreads();
+}
+
+template <int NT>
+__device__ __forceinline__ void load_hist_desc(const uint32_t* h, uint32_t (&cnt)[kBins / NT]) {
+  constexpr int kPer = kBins / NT;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) cnt[i] = h[kBins - 1 - (kPer * threadIdx.x + i)];
+}
+
+// Chunk candidates.  Every chunk of 1,024 blocks keeps, as 64-bit keys
+// (score, ~index) in its own region of the row's list, all its valid blocks
+// whose bin is at or above its local bin: the bin of its m-th best valid block
+// (all of them if it has fewer).  cinfo = count << 16 | local bin.  The
+// finalize takes the row's threshold bin T from the row histogram: a chunk
+// whose local bin is at most T has listed every block of bin >= T; one whose
+// local bin is above T is read again from its scores.  m is sized so that the
+// list usually fits the finalize's first round of loads (local_m).
+constexpr int kFinKeys = 8;  // candidate keys per finalize thread and round
+
+// Finalize threads per chunk in a round: as many as share the 512 threads, at
+// most kScoreChunk / kFinKeys (a round never reads past a chunk's list region).
+__device__ __forceinline__ int chunk_threads(int nb_stride) {
+  const int nch = min(nb_stride / kScoreChunk, 64);
+  int t = 1;
+  while (t * 2 * nch <= 512 && t * 2 * kFinKeys <= kScoreChunk) t *= 2;
+  return t;
+}
+__device__ __forceinline__ int local_m(int nb_stride) { return chunk_threads(nb_stride) * 4; }
+
+template <int NT, int IT>
+__device__ __forceinline__ void chunk_candidates(const uint32_t* hist, const int32_t (&sc)[IT], int c, int nb,
+                                                 int nb_stride, uint64_t* keys, uint32_t* cinfo, uint32_t* sh,
+                                                 int32_t* s_lb, uint32_t* s_tmp, uint32_t* s_cnt) {
+  constexpr int kPer = kBins / NT;
+  const int tid = threadIdx.x, l = lane_id();
+  const int valid_total = min(kScoreChunk, nb - c * kScoreChunk);
+  const uint32_t m = (uint32_t)min(local_m(nb_stride), valid_total);
+  uint32_t cnt[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) cnt[i] = hist[kBins - 1 - (kPer * tid + i)];
+  if (tid == 0) { *s_cnt = 0; *s_lb = 0; }
+  threshold_from_counts<NT>(cnt, m, sh, s_lb, s_tmp);
+  const int lb = *s_lb;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int j = c * kScoreChunk + it * NT + tid;
+    const bool take = j < nb && score_bin(sc[it]) >= lb;
+    const uint64_t mask = __ballot(take);
+    if (mask) {
+      uint32_t base = 0;
+      if (l == 0) base = atomicAdd(s_cnt, (uint32_t)__popcll(mask));
+      base = __shfl(base, 0, 64);
+      if (take) keys[base + (uint32_t)__popcll(mask & ((1ull << l) - 1ull))] = cand_key(sc[it], (uint32_t)j);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) *cinfo = (*s_cnt << 16) | (uint32_t)lb;
 }
 
 template <int D>
@@ -184,117 +280,103 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     const uint32_t h = hist[i];
     if (h) atomicAdd(&ghist[i], h);
   }
+  // this chunk's candidates for the finalize (no separate filter pass)
+  __shared__ uint32_t sh[kScoreThreads / 64];
+  __shared__ int32_t s_lb;
+  __shared__ uint32_t s_tmp, s_cnt;
+  chunk_candidates<kScoreThreads, kScoreIters>(hist, sc, c, nb, ws.nb_stride,
+                                               ws.keys + (size_t)s * ws.nb_stride + (size_t)c * kScoreChunk,
+                                               ws.cinfo + (size_t)s * (ws.nb_stride / kScoreChunk) + c, sh,
+                                               &s_lb, &s_tmp, &s_cnt);
 }
 
-// Block-wide exclusive prefix sum (blockDim.x threads, a multiple of 64).
-template <int NT>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh /*[NT/64]*/) {
-  const int l = lane_id(), w = threadIdx.x / 64;
-  const uint32_t inc = wave_incl_scan(v);
-  if (l == 63) sh[w] = inc;
-  __syncthreads();
-  uint32_t off = 0;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) off += (i < w) ? sh[i] : 0u;
-  __syncthreads();
-  return off + inc - v;
-}
-
-// Threshold bin from the row histogram: the bin T with
-// count(bins > T) < ks <= count(bins >= T).  Returns (T, count above T).
-template <int NT>
-__device__ __forceinline__ void find_threshold(const uint32_t* ghist, uint32_t ks, uint32_t* sh,
-                                               int32_t* s_T, uint32_t* s_above) {
-  constexpr int kPer = kBins / NT;
-  const int tid = threadIdx.x;
-  uint32_t cnt[kPer], mine = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    cnt[i] = ghist[kBins - 1 - (kPer * tid + i)];
-    mine += cnt[i];
-  }
-  uint32_t above = block_excl_scan<NT>(mine, sh);
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if (above < ks && above + cnt[i] >= ks) { *s_T = kBins - 1 - (kPer * tid + i); *s_above = above; }
-    above += cnt[i];
-  }
-  __syncthreads();
-}
-
-// Filter (grid: chunk x selecting row): blocks in bins above T -> bitmap words,
-// blocks in bin T -> candidate keys in this chunk's own region of the row's
-// list (LDS counter, no global atomics), then one count per chunk.
-__global__ __launch_bounds__(kThreads) void filter_kernel(
-    const int32_t* __restrict__ sel_seq_len, int32_t k, int32_t max_seq_len, WsPtrs ws) {
-  __shared__ uint32_t sh[kThreads / 64];
-  __shared__ int32_t s_T;
-  __shared__ uint32_t s_above;
-  __shared__ uint32_t s_cnt;
+// Chunk candidates from stored scores (grid: chunk x row; prefill, whose
+// scoring kernel covers 16 rows at a time): the chunk's histogram in LDS, then
+// the same candidate list as the decode scan writes.
+__global__ __launch_bounds__(kCandThreads) void chunk_cand_kernel(
+    const int32_t* __restrict__ sel_seq_len, int32_t max_seq_len, WsPtrs ws) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t sh[kCandThreads / 64];
+  __shared__ int32_t s_lb;
+  __shared__ uint32_t s_tmp, s_cnt;
   const int s = blockIdx.y;
   const int c = blockIdx.x;
   const int L = min(sel_seq_len[s], max_seq_len);
   const int nb = max(L, 0) >> 2;
-  const int nchunks = (nb + kScoreChunk - 1) / kScoreChunk;
-  if (c >= nchunks) return;
-  const int l = lane_id(), w = threadIdx.x / 64;
+  if (c * kScoreChunk >= nb) return;
   const int32_t* srow = ws.scores + (size_t)s * ws.nb_stride;
-  int32_t sc[kIters];  // unconditional loads: slots past the row's end exist and are masked
+  int32_t sc[kCandIters];  // unconditional loads: slots past the row's end exist and are masked
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) sc[it] = srow[c * kScoreChunk + it * kThreads + threadIdx.x];
-  if (threadIdx.x == 0) s_cnt = 0;
-  find_threshold<kThreads>(ws.hist + (size_t)s * kBins, (uint32_t)min(k, nb), sh, &s_T, &s_above);
-  const int T = s_T;
-  uint64_t* bm = ws.bitmap + (size_t)s * (ws.nb_stride / 64);
-  uint64_t* keys = ws.keys + (size_t)s * ws.nb_stride + (size_t)c * kScoreChunk;
+  for (int it = 0; it < kCandIters; ++it) sc[it] = srow[c * kScoreChunk + it * kCandThreads + threadIdx.x];
+  for (int i = threadIdx.x; i < kBins; i += kCandThreads) hist[i] = 0;
+  __syncthreads();
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int j0 = c * kScoreChunk + it * kThreads + w * 64;  // 64-aligned
-    const int j = j0 + l;
-    const bool valid = j < nb;
-    const int bin = score_bin(sc[it]);
-    const bool sure = valid && bin > T;
-    const bool maybe = valid && bin == T;
-    const uint64_t sure_mask = __ballot(sure);
-    const uint64_t maybe_mask = __ballot(maybe);
-    if (l == 0) bm[j0 >> 6] = sure_mask;
-    if (maybe_mask) {
-      uint32_t basepos = 0;
-      if (l == 0) basepos = atomicAdd(&s_cnt, (uint32_t)__popcll(maybe_mask));
-      basepos = __shfl(basepos, 0, 64);
-      if (maybe) keys[basepos + (uint32_t)__popcll(maybe_mask & ((1ull << l) - 1ull))] = cand_key(sc[it], (uint32_t)j);
-    }
+  for (int it = 0; it < kCandIters; ++it) {
+    const int j = c * kScoreChunk + it * kCandThreads + threadIdx.x;
+    atomicAdd(&hist[score_bin(sc[it])], j < nb ? 1u : 0u);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    ws.ccount[(size_t)s * (ws.nb_stride / kScoreChunk) + c] = s_cnt;
-    if (c == 0) { ws.meta[2 * s] = T; ws.meta[2 * s + 1] = (int32_t)s_above; }
-  }
+  chunk_candidates<kCandThreads, kCandIters>(hist, sc, c, nb, ws.nb_stride,
+                                             ws.keys + (size_t)s * ws.nb_stride + (size_t)c * kScoreChunk,
+                                             ws.cinfo + (size_t)s * (ws.nb_stride / kScoreChunk) + c, sh,
+                                             &s_lb, &s_tmp, &s_cnt);
 }
 
-// Finalize (one workgroup per selecting row): radix-select the missing blocks
-// among the threshold-bin candidates, set their bits, emit ascending ids.
+// Finalize (one workgroup per selecting row): the row's threshold bin T from
+// its histogram; the chunks' candidate lists (one round of loads, issued before
+// the row length is known) are classified: bin > T -> selected (LDS bitmap),
+// bin == T -> threshold candidates; the missing ones among those are picked
+// by an MSB-first radix select, and the bitmap is emitted in ascending order.
 constexpr int kFinThreads = 512;
-constexpr int kCandLds = 4096;   // candidates held in LDS (more: workspace)
+constexpr int kCandLds = 4096;   // threshold candidates held in LDS (more: workspace)
 constexpr int kWordsLds = 4096;  // bitmap words held in LDS (rows up to 262,144 blocks)
-constexpr int kSpec = 8;         // candidate keys per chunk loaded with the counts
 
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     const int32_t* __restrict__ sel_seq_len, int32_t k, int32_t max_seq_len,
     int32_t* __restrict__ topk, WsPtrs ws) {
+  constexpr int kPer = kBins / kFinThreads;
   __shared__ uint32_t sh[kFinThreads / 64];
   __shared__ __align__(16) uint32_t rhist[256];
   __shared__ uint64_t cand[kCandLds];
   __shared__ uint64_t bml[kWordsLds];
-  __shared__ uint32_t s_info[3];
-  __shared__ uint32_t s_off[kFinThreads];
+  __shared__ int32_t s_T;
+  __shared__ uint32_t s_above, s_n;
   __shared__ uint64_t s_sel[2];
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
-  const int L = min(sel_seq_len[s], max_seq_len);
+  const int nchunks_max = ws.nb_stride / kScoreChunk;
+  const int tpc = chunk_threads(ws.nb_stride);     // threads per chunk in a round
+  const int cpr = kFinThreads / tpc;               // chunks per round
+  const int sub = tid % tpc;
+  uint32_t* ghist = ws.hist + (size_t)s * kBins;
+  const uint32_t* cinfo = ws.cinfo + (size_t)s * nchunks_max;
+  const uint64_t* ckeys = ws.keys + (size_t)s * ws.nb_stride;
+  const int32_t* srow = ws.scores + (size_t)s * ws.nb_stride;
+  uint64_t* gkeys = ws.keys2 + (size_t)s * ws.nb_stride;
+  uint64_t* bm = ws.bitmap + (size_t)s * (ws.nb_stride / 64);
+
+  // First round, before the row length is known (clamped in bounds, masked
+  // below): the row histogram and, for the first cpr chunks, each chunk's
+  // cinfo and the first tpc * kFinKeys keys of its list.
+  uint32_t hc[kPer];
+  load_hist_desc<kFinThreads>(ghist, hc);
+  int cc = min(tid / tpc, nchunks_max - 1);
+  uint32_t ci = cinfo[cc];
+  uint64_t kk[kFinKeys];
+#pragma unroll
+  for (int e = 0; e < kFinKeys; ++e) kk[e] = ckeys[(size_t)cc * kScoreChunk + sub * kFinKeys + e];
+  const int Lr = sel_seq_len[s];
+  // keep the compiler from sinking those loads past the length test below
+  asm volatile("" ::"v"(ci), "s"(Lr));
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) asm volatile("" ::"v"(hc[i]));
+#pragma unroll
+  for (int e = 0; e < kFinKeys; ++e) asm volatile("" ::"v"(kk[e]));
+
+  const int L = min(Lr, max_seq_len);
   const int nb = max(L, 0) >> 2;
   int32_t* out = topk + (size_t)s * k;
-  if (nb == 0) {
+  if (nb == 0) {  // nothing was scored: the histogram is untouched
     for (int i = tid; i < k; i += kFinThreads) out[i] = -1;
     return;
   }
@@ -302,67 +384,66 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   const int nchunks = (nb + kScoreChunk - 1) / kScoreChunk;
   const int nwords = (nb + 63) >> 6;
   const bool bm_lds = nwords <= kWordsLds;
-  uint32_t* ghist = ws.hist + (size_t)s * kBins;
-  const uint32_t* ccnt = ws.ccount + (size_t)s * (ws.nb_stride / kScoreChunk);
-  const uint64_t* ckeys = ws.keys + (size_t)s * ws.nb_stride;
-  uint64_t* gkeys = ws.keys2 + (size_t)s * ws.nb_stride;
-  uint64_t* bm = ws.bitmap + (size_t)s * (ws.nb_stride / 64);
-
-  // The filter's bitmap of blocks above the threshold bin (into LDS), the
-  // count of blocks above the threshold bin, and per chunk the candidate
-  // count plus its first kSpec candidate keys: one round of loads.
-  if (bm_lds)
-    for (int i = tid; i < nwords; i += kFinThreads) bml[i] = bm[i];
-  const uint32_t above = (uint32_t)ws.meta[2 * s + 1];
-  uint32_t n = 0;
-  for (int c0 = 0; c0 < nchunks; c0 += kFinThreads) {
-    const int nc = min(kFinThreads, nchunks - c0);
-    uint32_t cnt = 0;
-    uint64_t spec[kSpec];
-    if (tid < nc) {
-      cnt = ccnt[c0 + tid];
-      const uint64_t* src = ckeys + (size_t)(c0 + tid) * kScoreChunk;
-#pragma unroll
-      for (int i = 0; i < kSpec; ++i) spec[i] = src[i];
-    }
-    const uint32_t excl = block_excl_scan<kFinThreads>(cnt, sh);
-    if (tid < nc) s_off[tid] = excl;
-    if (tid == kFinThreads - 1) s_info[0] = excl + cnt;
-#pragma unroll
-    for (int i = 0; i < kSpec; ++i) {
-      const uint32_t dst = n + excl + i;
-      if ((uint32_t)i < cnt) {
-        if (dst < (uint32_t)kCandLds) cand[dst] = spec[i];
-        else gkeys[dst] = spec[i];
-      }
-    }
-    __syncthreads();
-    const uint32_t round_n = s_info[0];
-    // chunks with more than kSpec candidates: copy the rest, one thread each
-    for (uint32_t i = tid; i < round_n; i += kFinThreads) {
-      int lo = 0, hi = nc - 1;  // last chunk with s_off <= i
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_off[mid] <= i) lo = mid; else hi = mid - 1;
-      }
-      const uint32_t r = i - s_off[lo];
-      if (r < (uint32_t)kSpec) continue;
-      const uint64_t key = ckeys[(size_t)(c0 + lo) * kScoreChunk + r];
-      const uint32_t dst = n + i;
-      if (dst < (uint32_t)kCandLds) cand[dst] = key;
-      else gkeys[dst] = key;
-    }
-    n += round_n;
-    __syncthreads();
+  if (bm_lds) {
+    for (int i = tid; i < nwords; i += kFinThreads) bml[i] = 0;
+  } else {
+    for (int i = tid; i < nwords; i += kFinThreads) bm[i] = 0;
   }
-  // the row histogram is consumed (the filter used it): clear it for the next call
-  for (int i = tid; i < kBins; i += kFinThreads) ghist[i] = 0;
+  if (tid == 0) { s_n = 0; s_T = 0; s_above = 0; }
+  threshold_from_counts<kFinThreads>(hc, ks, sh, &s_T, &s_above);
+  // the row histogram is consumed: clear it for the next call (each thread the bins it read)
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) ghist[kBins - 1 - (kPer * tid + i)] = 0;
+  const int T = s_T;
+  const uint32_t above = s_above;
+
+  auto mark = [&](uint32_t j) {
+    if (bm_lds) atomicOr(reinterpret_cast<unsigned long long*>(&bml[j >> 6]), 1ull << (j & 63));
+    else atomicOr(reinterpret_cast<unsigned long long*>(&bm[j >> 6]), 1ull << (j & 63));
+  };
+  auto classify = [&](uint64_t key) {
+    const int bin = score_bin(key_score(key));
+    if (bin > T) {
+      mark(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+    } else if (bin == T) {
+      const uint32_t i = atomicAdd(&s_n, 1u);
+      if (i < (uint32_t)kCandLds) cand[i] = key;
+      else gkeys[i] = key;
+    }
+  };
+  for (int c0 = 0; c0 < nchunks; c0 += cpr) {
+    const int c = c0 + tid / tpc;
+    if (c0 > 0) {  // rows of more than cpr chunks: further rounds
+      cc = min(c, nchunks_max - 1);
+      ci = cinfo[cc];
+#pragma unroll
+      for (int e = 0; e < kFinKeys; ++e) kk[e] = ckeys[(size_t)cc * kScoreChunk + sub * kFinKeys + e];
+    }
+    if (c < nchunks) {
+      const uint32_t cnt = ci >> 16;
+      const int lb = (int)(ci & 0xffffu);
+      if (lb <= T) {  // the list holds every block of this chunk with bin >= T
+#pragma unroll
+        for (int e = 0; e < kFinKeys; ++e)
+          if ((uint32_t)(sub * kFinKeys + e) < cnt) classify(kk[e]);
+        for (uint32_t i = (uint32_t)(tpc * kFinKeys + sub); i < cnt; i += tpc)
+          classify(ckeys[(size_t)c * kScoreChunk + i]);
+      } else {  // local bin above T: blocks of bins [T, lb) are not listed; read the chunk's scores
+        for (int i = sub; i < kScoreChunk; i += tpc) {
+          const int j = c * kScoreChunk + i;
+          if (j < nb) classify(cand_key(srow[j], (uint32_t)j));
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t n = s_n;
   const uint32_t need = ks - above;  // 1 <= need <= n
   auto key_at = [&](uint32_t i) -> uint64_t { return i < (uint32_t)kCandLds ? cand[i] : gkeys[i]; };
 
-  // MSB-first radix select of the need-th largest candidate key, by wave 0
-  // alone (no workgroup barriers inside).  All candidates share the threshold
-  // bin, i.e. key bits 46..63, so the digits start at bit 40.
+  // MSB-first radix select of the need-th largest threshold candidate, by
+  // wave 0 alone (no workgroup barriers inside).  All of them share the
+  // threshold bin, i.e. key bits 46..63, so the digits start at bit 40.
   constexpr uint64_t kBinMask = ~((1ull << (32 + kBinShift)) - 1ull);
   if (tid < 64 && need < n) {
     const int l = tid;
@@ -412,11 +493,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   const uint64_t prefix = s_sel[0], mask = s_sel[1];
   for (uint32_t i = tid; i < n; i += kFinThreads) {
     const uint64_t key = key_at(i);
-    if ((key & mask) >= prefix) {
-      const uint32_t j = 0xffffffffu - (uint32_t)(key & 0xffffffffull);
-      if (bm_lds) atomicOr(reinterpret_cast<unsigned long long*>(&bml[j >> 6]), 1ull << (j & 63));
-      else atomicOr(reinterpret_cast<unsigned long long*>(&bm[j >> 6]), 1ull << (j & 63));
-    }
+    if ((key & mask) >= prefix) mark(0xffffffffu - (uint32_t)(key & 0xffffffffull));
   }
   __syncthreads();
 
@@ -448,8 +525,9 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
 // score = q.s + 256 q.h - 384 sum(q) exactly in int32.  The B operand of lane l
 // is the 16-byte s-plane chunk l/16 of block l%16: a plain 16-byte load from
 // the page, no LDS.  Per-row histograms (16-bit counts, two per LDS word) are
-// merged into the rows' histograms as in the decode scan; the filter and
-// finalize kernels then select exactly as for qsa_index_topk.
+// merged into the rows' histograms as in the decode scan; a chunk-candidate
+// kernel then writes the chunks' candidate lists from the stored scores, and
+// the finalize selects exactly as for qsa_index_topk.
 constexpr int kPfThreads = 256;
 constexpr int kPfRows = 16;
 constexpr int kPfTiles = kScoreChunk / (kPfThreads / 64) / 16;  // block tiles per wave
@@ -599,8 +677,7 @@ TopkWorkspace topk_workspace_layout(int32_t rows, int32_t max_seq_len) {
   w.off_bitmap = off; off = al(off + (size_t)rows * (w.nb_stride / 64) * 8);
   w.off_keys2 = off;  off = al(off + (size_t)rows * w.nb_stride * 8);
   w.off_hist = off;   off = al(off + (size_t)rows * kBins * 4);
-  w.off_ccount = off; off = al(off + (size_t)rows * (w.nb_stride / kScoreChunk) * 4);
-  w.off_meta = off;   off = al(off + (size_t)rows * 2 * 4);
+  w.off_cinfo = off;  off = al(off + (size_t)rows * (w.nb_stride / kScoreChunk) * 4);
   w.total = off;
   return w;
 }
@@ -628,8 +705,7 @@ qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len
   ws.bitmap = reinterpret_cast<uint64_t*>(base + lay.off_bitmap);
   ws.keys2 = reinterpret_cast<uint64_t*>(base + lay.off_keys2);
   ws.hist = reinterpret_cast<uint32_t*>(base + lay.off_hist);
-  ws.ccount = reinterpret_cast<uint32_t*>(base + lay.off_ccount);
-  ws.meta = reinterpret_cast<int32_t*>(base + lay.off_meta);
+  ws.cinfo = reinterpret_cast<uint32_t*>(base + lay.off_cinfo);
   ws.nb_stride = lay.nb_stride;
   const int page_log2 = __builtin_ctz((unsigned)c.page_size);
   const int chunks = lay.nb_stride / kScoreChunk;
@@ -652,10 +728,6 @@ qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len
   }
   qsa_status st = check_launch("qsa_index_topk(score)");
   if (st != QSA_OK || topk == nullptr) return st;
-  hipLaunchKernelGGL(filter_kernel, grid, dim3(kThreads), 0, stream, sel_seq_len, c.topk_blocks,
-                     max_seq_len, ws);
-  st = check_launch("qsa_index_topk(filter)");
-  if (st != QSA_OK) return st;
   hipLaunchKernelGGL(finalize_kernel, dim3(S), dim3(kFinThreads), 0, stream, sel_seq_len, c.topk_blocks,
                      max_seq_len, topk, ws);
   return check_launch("qsa_index_topk(finalize)");
@@ -674,8 +746,7 @@ qsa_status launch_prefill_index_topk(const qsa_config& c, int32_t B, int32_t R, 
   ws.bitmap = reinterpret_cast<uint64_t*>(base + lay.off_bitmap);
   ws.keys2 = reinterpret_cast<uint64_t*>(base + lay.off_keys2);
   ws.hist = reinterpret_cast<uint32_t*>(base + lay.off_hist);
-  ws.ccount = reinterpret_cast<uint32_t*>(base + lay.off_ccount);
-  ws.meta = reinterpret_cast<int32_t*>(base + lay.off_meta);
+  ws.cinfo = reinterpret_cast<uint32_t*>(base + lay.off_cinfo);
   ws.nb_stride = lay.nb_stride;
   const int page_log2 = __builtin_ctz((unsigned)c.page_size);
   const int chunks = lay.nb_stride / kScoreChunk;
@@ -698,9 +769,9 @@ qsa_status launch_prefill_index_topk(const qsa_config& c, int32_t B, int32_t R, 
   }
   qsa_status st = check_launch("qsa_prefill_index_topk(score)");
   if (st != QSA_OK || topk == nullptr) return st;
-  hipLaunchKernelGGL(filter_kernel, dim3(chunks, R), dim3(kThreads), 0, stream, row_seq_len, c.topk_blocks,
+  hipLaunchKernelGGL(chunk_cand_kernel, dim3(chunks, R), dim3(kCandThreads), 0, stream, row_seq_len,
                      max_seq_len, ws);
-  st = check_launch("qsa_prefill_index_topk(filter)");
+  st = check_launch("qsa_prefill_index_topk(candidates)");
   if (st != QSA_OK) return st;
   hipLaunchKernelGGL(finalize_kernel, dim3(R), dim3(kFinThreads), 0, stream, row_seq_len, c.topk_blocks,
                      max_seq_len, topk, ws);

@@ -20,12 +20,11 @@ struct TopkWorkspace {
   int32_t rows;        // selecting rows it is sized for
   int32_t nb_stride;   // micro-block capacity per row (multiple of the chunk)
   size_t off_scores;   // int32  [rows][nb_stride]
-  size_t off_keys;     // uint64 [rows][nb_stride]  threshold-bin candidates, per chunk
-  size_t off_keys2;    // uint64 [rows][nb_stride]  the same, compacted
-  size_t off_bitmap;   // uint64 [rows][nb_stride/64]
-  size_t off_hist;     // uint32 [rows][kBins]  (all zero between calls)
-  size_t off_ccount;   // uint32 [rows][nb_stride/1024]  candidates per chunk
-  size_t off_meta;     // int32  [rows][2]  threshold bin, count of blocks above it
+  size_t off_keys;     // uint64 [rows][nb_stride]  each chunk's candidate list, in the chunk's region
+  size_t off_bitmap;   // uint64 [rows][nb_stride/64]  (rows too long for the finalize's LDS)
+  size_t off_keys2;    // uint64 [rows][nb_stride]  threshold candidates beyond the finalize's LDS
+  size_t off_hist;     // uint32 [rows][kBins]  (all zero between selecting calls)
+  size_t off_cinfo;    // uint32 [rows][nb_stride/1024]  per chunk: candidate count << 16 | local bin
   size_t total;
 };
 
