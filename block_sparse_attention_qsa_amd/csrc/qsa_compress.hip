@@ -13,9 +13,11 @@
 //
 // Work split: one grid row (blockIdx.y) per request, workgroups stride over the
 // micro-blocks that close in this call.  Only the block that straddles the
-// previous call (first block, when seq_len_before % 4 != 0) reads the ring, and
-// only the new tokens of the block left open write it; both happen in
-// workgroup 0, reads before writes, so any number of new tokens is race-free.
+// previous call (first block, when seq_len_before % 4 != 0) reads the ring;
+// the last (up to 8) new tokens are written to it, closed or not, so that a
+// caller can roll rejected draft tokens back (the pages' MTP flow: later draft
+// steps keep updating the side cache).  Reads and writes happen in workgroup
+// 0, reads first, so any number of new tokens is race-free.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -80,9 +82,9 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
   }
 
   if (blockIdx.x != 0) return;
-  // New tokens of the block left open go to the ring, after every ring read above.
+  // The last kRing new tokens go to the ring, after every ring read above.
   __syncthreads();
-  const int t0 = max(L0, 4 * jE);
+  const int t0 = max(L0, L0 + n - kRing);
   for (int i = threadIdx.x; i < (L0 + n - t0) * kGroups; i += kThreads) {
     const int t = t0 + i / kGroups;
     const int g = i % kGroups;

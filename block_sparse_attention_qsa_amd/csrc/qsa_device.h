@@ -9,7 +9,7 @@
 namespace qsa {
 
 constexpr int kRatio = 4;   // tokens per micro-block
-constexpr int kRing = 4;    // ring slots: one per token of the open micro-block
+constexpr int kRing = 8;    // ring slots (slot t % 8): the last 8 tokens' raw keys
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));

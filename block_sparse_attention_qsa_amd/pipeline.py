@@ -53,7 +53,7 @@ class QSALayer:
         fill = (lambda t: t.fill_(0x7F) if t.dtype == torch.int8 else t.fill_(float("nan"))) if poison \
             else (lambda t: t.zero_())
         self.ckey = fill(torch.empty(api.ckey_cache_bytes(self.cfg, wl.num_pages), dtype=torch.int8, device=dev))
-        self.ring = fill(torch.empty((B, 4, s.index_dim), dtype=torch.int8, device=dev))
+        self.ring = fill(torch.empty((B, 8, s.index_dim), dtype=torch.int8, device=dev))
         self.max_seq_len = int(max_seq_len if max_seq_len is not None else int(wl.final_len.max()))
         ws_bytes = api.qsa_index_topk_workspace_size(self.cfg, S, self.max_seq_len)
         self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)

@@ -55,8 +55,8 @@
  *                [16r, 16r+16) of every slot), then per slot D/4 mask bytes (b0 of
  *                dims 0..D-1, then b1; dim i is bit i%8 of byte i/8).
  *                Size: qsa_ckey_cache_bytes().
- *   ring         int8 [num_reqs, 4, D]: the keys of each request's open micro-block
- *                (slot t % 4).  Only slots of the open block are ever read.
+ *   ring         int8 [num_reqs, 8, D]: the raw keys of each request's last 8
+ *                tokens (slot t % 8).  Only the open block's tokens are ever read.
  */
 #ifndef QSA_H_
 #define QSA_H_
@@ -109,9 +109,16 @@ size_t qsa_ckey_cache_bytes(const qsa_config* cfg, int64_t num_pages);
  * new_keys (int8 [T_new, D]) as tokens seq_len_before[b], seq_len_before[b]+1, ...
  * Every micro-block j whose last token 4j+3 is among them gets
  * C_j = k_{4j} + k_{4j+1} + k_{4j+2} + k_{4j+3} written to ckey_cache; keys of
- * tokens before seq_len_before[b] that C_j needs come from ring[b]; the new
- * tokens of the block left open are written to ring[b].  Any number of new
- * tokens and any seq_len_before are handled (bulk prefill and decode alike).
+ * tokens before seq_len_before[b] that C_j needs come from ring[b]; the last
+ * (up to 8) new tokens are written to ring[b].  Any number of new tokens and
+ * any seq_len_before are handled (bulk prefill and decode alike).
+ * Rollback ([PR53896]: MTP draft steps keep updating the side cache, and
+ * rejected draft tokens must not stay in it): a call may restart from an
+ * earlier length L (seq_len_before[b] = L after the caller drops rejected
+ * tokens) if the last call that wrote request b ended at most
+ * 4*floor(L/4) + 8 tokens in, i.e. up to 8 - L%4 (>= 5) tokens are dropped.
+ * Blocks that the dropped tokens closed are rewritten when they close again;
+ * scans never read them before (they lie past floor(L/4)).
  * Requests with seq_len_before[b] < 0 or no new tokens write nothing
  * ([QSA-DCP]: dummy batches must not write the side cache).
  *   max_new_tokens: host-side upper bound of new_cu[b+1]-new_cu[b] (sizes the grid;

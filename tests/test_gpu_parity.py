@@ -70,8 +70,8 @@ def test_compress_incremental_equals_bulk(chunk):
     for b in range(wl.num_reqs):
         L = int(wl.prefix_len[b])
         for t in range(4 * (L // 4), L):
-            assert np.array_equal(rb[b, t % 4], keys[wl.key_off[b] + t])
-            assert np.array_equal(ri[b, t % 4], keys[wl.key_off[b] + t])
+            assert np.array_equal(rb[b, t % 8], keys[wl.key_off[b] + t])
+            assert np.array_equal(ri[b, t % 8], keys[wl.key_off[b] + t])
 
 
 def test_compress_skips_dummy_requests():
