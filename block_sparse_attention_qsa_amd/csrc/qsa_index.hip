@@ -110,7 +110,8 @@ __device__ __forceinline__ void load_hist_desc(const uint32_t* h, uint32_t (&cnt
 // finalize takes the row's threshold bin T from the row histogram: a chunk
 // whose local bin is at most T has listed every block of bin >= T; one whose
 // local bin is above T is read again from its scores.  m is sized so that the
-// list usually fits the finalize's first round of loads (local_m).
+// list usually fits the finalize's first round of loads (local_m).  The local
+// bin is found by one wave walking down from the chunk's highest bin.
 constexpr int kFinKeys = 8;  // candidate keys per finalize thread and round
 
 // Finalize threads per chunk in a round: as many as share the 512 threads, at
@@ -124,18 +125,35 @@ __device__ __forceinline__ int chunk_threads(int nb_stride) {
 __device__ __forceinline__ int local_m(int nb_stride) { return chunk_threads(nb_stride) * 4; }
 
 template <int NT, int IT>
-__device__ __forceinline__ void chunk_candidates(const uint32_t* hist, const int32_t (&sc)[IT], int c, int nb,
-                                                 int nb_stride, uint64_t* keys, uint32_t* cinfo, uint32_t* sh,
-                                                 int32_t* s_lb, uint32_t* s_tmp, uint32_t* s_cnt) {
-  constexpr int kPer = kBins / NT;
+__device__ __forceinline__ void chunk_candidates(const uint32_t* hist, int maxbin, const int32_t (&sc)[IT], int c,
+                                                 int nb, int nb_stride, uint64_t* keys, uint32_t* cinfo,
+                                                 int32_t* s_lb, uint32_t* s_cnt) {
   const int tid = threadIdx.x, l = lane_id();
   const int valid_total = min(kScoreChunk, nb - c * kScoreChunk);
   const uint32_t m = (uint32_t)min(local_m(nb_stride), valid_total);
-  uint32_t cnt[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) cnt[i] = hist[kBins - 1 - (kPer * tid + i)];
-  if (tid == 0) { *s_cnt = 0; *s_lb = 0; }
-  threshold_from_counts<NT>(cnt, m, sh, s_lb, s_tmp);
+  // The local bin, by wave 0 alone: 64 bins at a time downward from the
+  // chunk's highest occupied bin (one step, as a rule); the count of all bins
+  // is valid_total >= m, so the walk ends before bin 0.
+  if (tid < 64) {
+    int top = maxbin, lb = 0;
+    uint32_t acc = 0;
+    bool found = false;
+    while (!found && top >= 0) {
+      const int bin = top - l;
+      const uint32_t cnt = bin >= 0 ? hist[bin] : 0u;
+      const uint32_t inc = wave_incl_scan(cnt) + acc;
+      const uint64_t hit = __ballot(inc >= m);
+      if (hit) {
+        found = true;
+        lb = top - (__ffsll((long long)hit) - 1);
+      } else {
+        acc = __shfl(inc, 63, 64);
+        top -= 64;
+      }
+    }
+    if (l == 0) { *s_lb = lb; *s_cnt = 0; }
+  }
+  __syncthreads();
   const int lb = *s_lb;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -151,6 +169,21 @@ __device__ __forceinline__ void chunk_candidates(const uint32_t* hist, const int
   }
   __syncthreads();
   if (tid == 0) *cinfo = (*s_cnt << 16) | (uint32_t)lb;
+}
+
+// Highest bin of this thread's valid scores, merged into s_maxbin (one LDS
+// atomic per wave).
+template <int IT>
+__device__ __forceinline__ void note_max_bin(const int32_t (&sc)[IT], int c, int nt, int nb, int* s_maxbin) {
+  int mb = -1;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int j = c * kScoreChunk + it * nt + (int)threadIdx.x;
+    mb = max(mb, j < nb ? score_bin(sc[it]) : -1);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mb = max(mb, __shfl_xor(mb, o, 64));
+  if (lane_id() == 0) atomicMax(s_maxbin, mb);
 }
 
 template <int D>
@@ -236,7 +269,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
       if (2 * h + 1 < kMaskWords) qp[t][2 * h + 1] = (uint32_t)(m >> 32);
     }
   }
+  __shared__ int s_maxbin;
   for (int i = threadIdx.x; i < kBins; i += kScoreThreads) hist[i] = 0;
+  if (threadIdx.x == 0) s_maxbin = -1;
   int32_t sc[kScoreIters];
 #pragma unroll
   for (int it = 0; it < kScoreIters; ++it) {
@@ -267,6 +302,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     const int j = c * kScoreChunk + it * kScoreThreads + threadIdx.x;
     atomicAdd(&hist[score_bin(sc[it])], j < nb ? 1u : 0u);
   }
+  note_max_bin<kScoreIters>(sc, c, kScoreThreads, nb, &s_maxbin);
   __syncthreads();
   // No branches here either: the workspace has score slots up to the chunk's
   // end (slots past the row's end are never read).  The per-row histogram is
@@ -281,13 +317,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     if (h) atomicAdd(&ghist[i], h);
   }
   // this chunk's candidates for the finalize (no separate filter pass)
-  __shared__ uint32_t sh[kScoreThreads / 64];
   __shared__ int32_t s_lb;
-  __shared__ uint32_t s_tmp, s_cnt;
-  chunk_candidates<kScoreThreads, kScoreIters>(hist, sc, c, nb, ws.nb_stride,
+  __shared__ uint32_t s_cnt;
+  chunk_candidates<kScoreThreads, kScoreIters>(hist, s_maxbin, sc, c, nb, ws.nb_stride,
                                                ws.keys + (size_t)s * ws.nb_stride + (size_t)c * kScoreChunk,
-                                               ws.cinfo + (size_t)s * (ws.nb_stride / kScoreChunk) + c, sh,
-                                               &s_lb, &s_tmp, &s_cnt);
+                                               ws.cinfo + (size_t)s * (ws.nb_stride / kScoreChunk) + c,
+                                               &s_lb, &s_cnt);
 }
 
 // Chunk candidates from stored scores (grid: chunk x row; prefill, whose
@@ -296,9 +331,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
 __global__ __launch_bounds__(kCandThreads) void chunk_cand_kernel(
     const int32_t* __restrict__ sel_seq_len, int32_t max_seq_len, WsPtrs ws) {
   __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t sh[kCandThreads / 64];
   __shared__ int32_t s_lb;
-  __shared__ uint32_t s_tmp, s_cnt;
+  __shared__ uint32_t s_cnt;
+  __shared__ int s_maxbin;
   const int s = blockIdx.y;
   const int c = blockIdx.x;
   const int L = min(sel_seq_len[s], max_seq_len);
@@ -309,17 +344,19 @@ __global__ __launch_bounds__(kCandThreads) void chunk_cand_kernel(
 #pragma unroll
   for (int it = 0; it < kCandIters; ++it) sc[it] = srow[c * kScoreChunk + it * kCandThreads + threadIdx.x];
   for (int i = threadIdx.x; i < kBins; i += kCandThreads) hist[i] = 0;
+  if (threadIdx.x == 0) s_maxbin = -1;
   __syncthreads();
 #pragma unroll
   for (int it = 0; it < kCandIters; ++it) {
     const int j = c * kScoreChunk + it * kCandThreads + threadIdx.x;
     atomicAdd(&hist[score_bin(sc[it])], j < nb ? 1u : 0u);
   }
+  note_max_bin<kCandIters>(sc, c, kCandThreads, nb, &s_maxbin);
   __syncthreads();
-  chunk_candidates<kCandThreads, kCandIters>(hist, sc, c, nb, ws.nb_stride,
+  chunk_candidates<kCandThreads, kCandIters>(hist, s_maxbin, sc, c, nb, ws.nb_stride,
                                              ws.keys + (size_t)s * ws.nb_stride + (size_t)c * kScoreChunk,
-                                             ws.cinfo + (size_t)s * (ws.nb_stride / kScoreChunk) + c, sh,
-                                             &s_lb, &s_tmp, &s_cnt);
+                                             ws.cinfo + (size_t)s * (ws.nb_stride / kScoreChunk) + c,
+                                             &s_lb, &s_cnt);
 }
 
 // Finalize (one workgroup per selecting row): the row's threshold bin T from
