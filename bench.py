@@ -323,6 +323,64 @@ def prefill_bench(args):
     print(json.dumps(res))
 
 
+def frontend_bench(args):
+    """The indexer front end (qsa_indexer_project) at a decode step (8 tokens) and a
+    prefill chunk (2,048 tokens), hidden size 4,096, D = 64; one JSON line."""
+    import torch
+
+    from block_sparse_attention_qsa_amd import api
+    H, D = 4096, 64
+    stream = torch.cuda.Stream()
+    out = {}
+    for T in (8, 2048):
+        g = torch.Generator(device="cuda").manual_seed(11 + T)
+        nl = 8  # rotate over independent inputs so each launch reads cold data
+        hs = [torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16) for _ in range(nl)]
+        ws = [(torch.randn((2 * D, H), generator=g, device="cuda") / H ** 0.5).to(torch.bfloat16) for _ in range(nl)]
+        gq = torch.zeros(D, device="cuda")
+        gk = torch.zeros(D, device="cuda")
+        pos = torch.arange(T, dtype=torch.int32, device="cuda")
+        q = torch.empty((T, D), dtype=torch.int8, device="cuda")
+        k = torch.empty((T, D), dtype=torch.int8, device="cuda")
+        scratch = torch.empty(max(api.qsa_indexer_project_workspace_size(T, H, D), 16), dtype=torch.uint8,
+                              device="cuda")
+
+        def run():
+            for i in range(nl):
+                api.qsa_indexer_project(hs[i], pos, ws[i], gq, gk, q, k, workspace=scratch, stream=stream)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            run()
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            for _ in range(args.steps):
+                graph.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (args.steps * nl)
+        nbytes = T * H * 2 + 2 * D * H * 2 + T * 4 + 2 * T * D
+        flops = 2.0 * T * H * 2 * D
+        out[f"T{T}"] = {"us_per_launch": us, "tokens_per_s": T / (us * 1e-6),
+                        "hbm_GBps": nbytes / (us * 1e-6) / 1e9, "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                        "bf16_TFLOPs": flops / (us * 1e-6) / 1e12, "bytes": nbytes}
+    big = out["T2048"]
+    res = {"metric": "QSA indexer front end tokens/s (projection + RMSNorm + rotary + int8)",
+           "value": big["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "hidden 4,096 -> D=64 query and key, bf16 weights [128, 4,096]; "
+                                  "2,048 tokens (prefill chunk) and 8 tokens (decode step)"},
+           "roofline": {"kernel": "qsa::project_kernel<64> (bf16 MFMA projection + fused epilogue)", "bound": "hbm",
+                        "achieved": big["hbm_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": big["hbm_frac"], "traffic": None, "bytes_per_launch": big["bytes"],
+                        "avg_launch_us": big["us_per_launch"]},
+           "sizes": out}
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +396,8 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
     ap.add_argument("--prefill", action="store_true",
                     help="measure the chunked-prefill path instead (its own JSON line)")
+    ap.add_argument("--frontend", action="store_true",
+                    help="measure the indexer front end instead (its own JSON line)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -357,6 +417,9 @@ def main():
         return
     if args.prefill:
         prefill_bench(args)
+        return
+    if args.frontend:
+        frontend_bench(args)
         return
     from block_sparse_attention_qsa_amd import api
     from block_sparse_attention_qsa_amd.pipeline import QSALayer

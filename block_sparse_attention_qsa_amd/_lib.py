@@ -53,6 +53,9 @@ SIGNATURES = {
     "qsa_prefill_index_topk": (_I, [_CFG, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "qsa_sparse_decode": (_I, [_CFG, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "qsa_merge_partials": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P]),
+    "qsa_indexer_project_workspace_size": (ctypes.c_size_t, [_I, _I, _I]),
+    "qsa_indexer_project": (_I, [_I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                 _P, _P, _P, ctypes.c_size_t, _P]),
     "qsa_status_string": (ctypes.c_char_p, [_I]),
     "qsa_last_error": (ctypes.c_char_p, []),
     "qsa_version": (ctypes.c_char_p, []),

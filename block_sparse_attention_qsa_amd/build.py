@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqsa.so")
 
-SOURCES = ["qsa_api.cpp", "qsa_compress.hip", "qsa_index.hip", "qsa_decode.hip"]
+SOURCES = ["qsa_api.cpp", "qsa_compress.hip", "qsa_index.hip", "qsa_decode.hip", "qsa_frontend.hip"]
 # the streaming-ceiling kernel bench.py reports beside the scan: its own library
 CEILING_SOURCES = ["qsa_stream_ceiling.hip"]
 CEILING_LIB = os.path.join(PKG, "libqsa_ceiling.so")

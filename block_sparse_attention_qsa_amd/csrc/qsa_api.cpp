@@ -1,6 +1,7 @@
 // Host entry points of libqsa.so: argument validation, then kernel launches.
 // Every check runs before anything is enqueued; see include/qsa.h for the
 // contract of each call.
+#include <cmath>
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -219,6 +220,41 @@ qsa_status qsa_merge_partials(int32_t num_splits, int32_t num_rows, int32_t num_
     return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_merge_partials: NULL array argument");
   return launch_merge(num_splits, num_rows, num_heads, head_dim, o_part, lse_part, out,
                       out_dtype == QSA_OUT_BF16, lse, stream);
+}
+
+size_t qsa_indexer_project_workspace_size(int32_t num_tokens, int32_t hidden_dim, int32_t index_dim) {
+  if (num_tokens < 0 || num_tokens > (1 << 24) || hidden_dim < 32 || hidden_dim % 32 != 0 || hidden_dim > 65536 ||
+      (index_dim != 32 && index_dim != 64 && index_dim != 128))
+    return 0;
+  return qsa::indexer_project_workspace_bytes(num_tokens, hidden_dim, index_dim);
+}
+
+qsa_status qsa_indexer_project(int32_t num_tokens, int32_t hidden_dim, int32_t index_dim, const void* hidden,
+                               const int32_t* positions, const void* w_qk, const float* g_q, const float* g_k,
+                               float rope_base, float q_scale, float k_scale, int8_t* q_index, int8_t* keys,
+                               void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (num_tokens < 0 || num_tokens > (1 << 24))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "num_tokens must be in [0, 2^24] (got %d)", num_tokens);
+  if (hidden_dim < 32 || hidden_dim % 32 != 0 || hidden_dim > 65536)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "hidden_dim must be a multiple of 32 in [32, 65536] (got %d)", hidden_dim);
+  if (index_dim != 32 && index_dim != 64 && index_dim != 128)
+    return fail(QSA_ERR_UNSUPPORTED, "index_dim %d not built (32, 64, 128)", index_dim);
+  if (!(rope_base > 1.0f) || !(q_scale > 0.0f) || !(k_scale > 0.0f) || !std::isfinite(rope_base) ||
+      !std::isfinite(q_scale) || !std::isfinite(k_scale))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "rope_base must be > 1 and the scales > 0, all finite");
+  if (num_tokens == 0) return QSA_OK;
+  if (!hidden || !positions || !w_qk || !g_q || !g_k || !q_index || !keys)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_indexer_project: NULL array argument");
+  if (!aligned(hidden, 16) || !aligned(w_qk, 16) || !aligned(q_index, 4) || !aligned(keys, 4))
+    return fail(QSA_ERR_INVALID_ARGUMENT,
+                "qsa_indexer_project: hidden and w_qk need 16-byte, q_index and keys 4-byte alignment");
+  if (!workspace || !aligned(workspace, 16))
+    return fail(QSA_ERR_WORKSPACE, "qsa_indexer_project: workspace is NULL or not 16-byte aligned");
+  const size_t need = indexer_project_workspace_bytes(num_tokens, hidden_dim, index_dim);
+  if (ws_bytes < need)
+    return fail(QSA_ERR_WORKSPACE, "qsa_indexer_project: workspace has %zu bytes, needs %zu", ws_bytes, need);
+  return launch_indexer_project(num_tokens, hidden_dim, index_dim, hidden, positions, w_qk, g_q, g_k, rope_base,
+                                q_scale, k_scale, q_index, keys, reinterpret_cast<float*>(workspace), stream);
 }
 
 const char* qsa_status_string(qsa_status s) {

@@ -53,6 +53,12 @@ qsa_status launch_prefill_index_topk(const qsa_config& c, int32_t B, int32_t R, 
 
 qsa_status launch_ws_clear(void* ws, size_t bytes, hipStream_t stream);
 
+size_t indexer_project_workspace_bytes(int32_t T, int32_t H, int32_t D);
+
+qsa_status launch_indexer_project(int32_t T, int32_t H, int32_t D, const void* hidden, const int32_t* positions,
+                                  const void* w_qk, const float* g_q, const float* g_k, float base, float q_scale,
+                                  float k_scale, int8_t* q_index, int8_t* keys, float* ws, hipStream_t stream);
+
 qsa_status launch_sparse_decode(const qsa_config& c, int32_t S, int32_t q_per_sel, int32_t P,
                                 const void* q, const int32_t* row_seq_len, const int32_t* sel_req,
                                 const int32_t* sel_seq_len, const int32_t* topk,

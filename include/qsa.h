@@ -251,6 +251,33 @@ qsa_status qsa_merge_partials(int32_t num_splits, int32_t num_rows, int32_t num_
                               int32_t head_dim, const float* o_part, const float* lse_part,
                               void* out, int32_t out_dtype, float* lse, hipStream_t stream);
 
+/*
+ * qsa_indexer_project -- the indexer front end: hidden states to the int8
+ * indexer query and keys that qsa_index_topk / qsa_compress take.
+ * [PR53896] (key source snippets, QSAIndexer): Q and K are projected from the
+ * hidden states, normalised with a Gemma-style RMSNorm and rotated by a 1-D
+ * rotary embedding before K enters the raw-key ring and Q selects.  For token
+ * t at position positions[t]:
+ *   [q | k] = hidden[t] . w_qk^T     (w_qk bf16 [2D, H]: rows 0..D-1 give q, D..2D-1 give k)
+ *   x = x / sqrt(mean(x^2) + 1e-6) * (1 + g)            (g_q fp32 [D] for q, g_k for k)
+ *   (x_i, x_{i+D/2}) rotated by positions[t] * rope_base^(-2i/D), i < D/2
+ *   out = clamp(round-half-even(x * scale), -127, 127)  (q_scale, k_scale)
+ *   hidden bf16 [T, H] (H a multiple of 32), 16-byte aligned like w_qk;
+ *   q_index, keys int8 [T, D]; index_dim D in {32, 64, 128}.
+ * Sums are fp32 over bf16 products (slices of H summed in a fixed order, so
+ * results are deterministic): a value within ~1e-4 of a rounding boundary may
+ * round either way.
+ *   workspace: device scratch of at least
+ *   qsa_indexer_project_workspace_size(num_tokens, hidden_dim, index_dim) bytes,
+ *   16-byte aligned, no initialisation; calls sharing it must be ordered.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (index_dim), WORKSPACE, HIP.
+ */
+size_t qsa_indexer_project_workspace_size(int32_t num_tokens, int32_t hidden_dim, int32_t index_dim);
+qsa_status qsa_indexer_project(int32_t num_tokens, int32_t hidden_dim, int32_t index_dim, const void* hidden,
+                               const int32_t* positions, const void* w_qk, const float* g_q, const float* g_k,
+                               float rope_base, float q_scale, float k_scale, int8_t* q_index, int8_t* keys,
+                               void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Human-readable name of a status. */
 const char* qsa_status_string(qsa_status status);
 

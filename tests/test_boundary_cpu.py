@@ -159,3 +159,27 @@ def test_python_binding_raises_with_message():
     with pytest.raises(api.QSAError, match="page_size"):
         api._check(_lib.load().qsa_compress(ctypes.byref(bad.to_c()), 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
                                             FAKE, None))
+
+
+def test_indexer_project_rejects(lib):
+    n = lib.qsa_indexer_project_workspace_size(8, 256, 64)
+    assert n > 0 and lib.qsa_indexer_project_workspace_size(8, 48, 64) == 0
+    assert lib.qsa_indexer_project_workspace_size(8, 256, 96) == 0
+
+    def fe(T=8, H=256, D=64, h=FAKE, w=FAKE, base=10000.0, qs=32.0, ks=32.0, q=FAKE, k=FAKE, ws=FAKE, nbytes=n):
+        return lib.qsa_indexer_project(T, H, D, h, FAKE, w, FAKE, FAKE, base, qs, ks, q, k, ws, nbytes, None)
+    assert fe(ws=None) == 3
+    assert fe(nbytes=n - 1) == 3
+    assert fe(ws=ctypes.c_void_p(0x10004)) == 3
+    assert fe(T=-1) == 1
+    assert fe(H=48) == 1              # not a multiple of 32
+    assert fe(H=0) == 1
+    assert fe(D=48) == 2
+    assert fe(base=1.0) == 1
+    assert fe(qs=0.0) == 1
+    assert fe(ks=float("nan")) == 1
+    assert fe(h=None) == 1
+    assert fe(w=ctypes.c_void_p(0x10008)) == 1   # weights not 16-byte aligned
+    assert fe(q=ctypes.c_void_p(0x10002)) == 1
+    assert fe(T=0) == 0
+
