@@ -6,7 +6,9 @@ A step is one decode step of every layer in a stack of `--layers` independent
 QSA layers (default 12, the number of QSA layers in the 48-layer model the
 pages describe), each layer running the whole hot path on its own caches:
 
-    qsa_compress -> qsa_index_topk -> qsa_sparse_decode -> qsa_merge_partials
+    qsa_compress_index_topk -> qsa_sparse_decode -> qsa_merge_partials
+
+(--no-fuse: qsa_compress, then qsa_index_topk, for the separate calls)
 
 The per-layer caches (about 84 MB touched per layer at 256k context) rotate so
 that one step touches about 1 GB, far beyond the 256 MB Infinity Cache.  The
@@ -70,6 +72,16 @@ def algorithmic_bytes(wl):
     R = wl.num_rows
     attend += R * hq * d * 2 + R * hq * d * 4 + R * hq * 4
     return scan, attend
+
+
+def append_bytes(wl):
+    """Bytes of the step's append, per layer: the new keys, the ring slots of the
+    straddling block read, the new tokens' ring slots and the closed blocks written."""
+    D = wl.shape.index_dim
+    before = wl.prefix_len.astype(np.int64)
+    n = wl.final_len.astype(np.int64) - before
+    closed = (before + n) // 4 - before // 4
+    return int((n * D + (before % 4) * D + np.minimum(n, 8) * D + closed * (D + D // 4)).sum())
 
 
 def cpu_baseline(wl, seconds: float):
@@ -215,13 +227,16 @@ def stream_ceiling(stream, reps: int = 10):
             "bytes": nbytes, "GBps": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
 
 
-def measured_traffic():
+def measured_traffic(fused: bool):
     """HBM bytes per scan launch from the committed rocprofv3 counter summary,
-    or None when the kernel source has changed since the counters were taken."""
+    or None when the kernel source has changed since the counters were taken
+    (or they were taken for the other variant of the scan)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "score_kernel_long256k_hbm_counters.md")
     try:
         kv = dict(line.split(" = ", 1) for line in open(path).read().splitlines() if " = " in line)
+        if kv.get("variant", "separate").strip() != ("fused" if fused else "separate"):
+            return None
         src = os.path.join(ROOT, kv["kernel_source"].strip())
         if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["kernel_source_sha256"].strip():
             return None
@@ -390,6 +405,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--layers", type=int, default=12)
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="append with qsa_compress, then qsa_index_topk (two scans' worth of launches)")
     ap.add_argument("--kernel-iters", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -431,7 +448,7 @@ def main():
     layers = []
     for li in range(args.layers):
         wl = named_workload(cfg, device=dev, seed=None if li == 0 else 1000 * cfg + li)
-        layer = QSALayer(wl, num_splits=P)
+        layer = QSALayer(wl, num_splits=P, fuse_append=not args.no_fuse)
         layer.prefill()
         layers.append(layer)
         print(f"[bench] layer {li} ready ({wl.name}, rows={wl.num_rows})", file=sys.stderr, flush=True)
@@ -481,15 +498,24 @@ def main():
     marks = [e0] + evs + [e1]
     per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
 
-    # Dominant kernel: the compressed-key scan (qsa_index_topk with topk=None runs
-    # only that kernel).  Its launches for all layers, back to back, are captured
-    # in a graph and timed with HIP events on the launch stream; the layers rotate,
-    # so every launch streams its own (cold) compressed-key cache.
+    # Dominant kernel: the compressed-key scan, as the step runs it (with the
+    # step's append when fused; topk=None runs only the scan kernel; re-appending
+    # the same tokens rewrites the same bytes).  Its launches for all layers, back
+    # to back, are captured in a graph and timed with HIP events on the launch
+    # stream; the layers rotate, so every launch streams its own (cold) cache.
+    fused = layers[0].fused
+
     def scan_all():
         for layer in layers:
-            api.qsa_index_topk(layer.cfg, layer.wl.q_index, layer.wl.sel_req, layer.wl.sel_seq_len,
-                               layer.wl.block_table, layer.ckey, None, layer.workspace,
-                               layer.max_seq_len, stream=stream)
+            wl = layer.wl
+            if fused:
+                api.qsa_compress_index_topk(layer.cfg, layer.step_keys, layer.step_cu, layer.step_before,
+                                            layer.ring, wl.q_index, wl.sel_req, wl.sel_seq_len, wl.block_table,
+                                            layer.ckey, None, layer.workspace, layer.step_max_new,
+                                            layer.max_seq_len, stream=stream)
+            else:
+                api.qsa_index_topk(layer.cfg, wl.q_index, wl.sel_req, wl.sel_seq_len, wl.block_table,
+                                   layer.ckey, None, layer.workspace, layer.max_seq_len, stream=stream)
     kern_ms, n_launches = float("nan"), 0
     if args.kernel_iters > 0:
         kgraph = torch.cuda.CUDAGraph()
@@ -510,8 +536,9 @@ def main():
         kern_ms = ka.elapsed_time(kb) / n_launches
 
     scan_b, attend_b = zip(*[algorithmic_bytes(l.wl) for l in layers])
-    scan_per_launch = float(np.mean(scan_b))
-    step_bytes = float(sum(scan_b) + sum(attend_b))
+    app_b = [append_bytes(l.wl) for l in layers]
+    scan_per_launch = float(np.mean(scan_b)) + (float(np.mean(app_b)) if fused else 0.0)
+    step_bytes = float(sum(scan_b) + sum(attend_b) + sum(app_b))
     achieved = scan_per_launch / (kern_ms * 1e-3) / 1e9
     rows_s = rows_per_step / (ms * 1e-3)
 
@@ -532,14 +559,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"cfg{cfg} {DESCR[cfg]}", "layers_per_step": args.layers,
                    "query_rows_per_layer": wl0.num_rows, "splits": P, "hip_graph": graph is not None,
+                   "append": "fused into the scan" if fused else "separate qsa_compress launch",
                    "index_arith": "int8 dot4 -> int32 (exact)", "attention_arith": "bf16 MFMA / fp32 softmax"},
         "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
                      "frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "wall_s": t_wall},
-        "roofline": {"kernel": "qsa::score_kernel (qsa_index_topk compressed-key scan)", "bound": "hbm",
+        "roofline": {"kernel": ("qsa::score_kernel<D, true> (qsa_compress_index_topk: append + compressed-key scan)"
+                                if fused else "qsa::score_kernel<D, false> (qsa_index_topk compressed-key scan)"),
+                     "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic() if cfg == 3 else None,
+                     "traffic": measured_traffic(fused) if cfg == 3 else None,
                      "bytes_per_launch": scan_per_launch, "avg_launch_us": kern_ms * 1e3,
                      "launches_timed": n_launches},
     }

@@ -71,8 +71,8 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _dt(t: torch.Tensor, *dtypes) -> None:
-    if t.dtype not in dtypes:
+def _dt(t: Optional[torch.Tensor], *dtypes) -> None:
+    if t is not None and t.dtype not in dtypes:
         raise TypeError(f"expected dtype in {dtypes}, got {t.dtype}")
 
 
@@ -119,6 +119,25 @@ def qsa_index_topk(cfg: QSAConfig, q_index: torch.Tensor, sel_req: torch.Tensor,
                                       _ptr(sel_seq_len), _ptr(block_table), _ptr(ckey_cache),
                                       _ptr(topk), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def qsa_compress_index_topk(cfg: QSAConfig, new_keys: torch.Tensor, new_cu: torch.Tensor,
+                            seq_len_before: torch.Tensor, ring: torch.Tensor, q_index: torch.Tensor,
+                            sel_req: torch.Tensor, sel_seq_len: torch.Tensor, block_table: torch.Tensor,
+                            ckey_cache: torch.Tensor, topk: torch.Tensor, workspace: torch.Tensor,
+                            max_new_tokens: int, max_seq_len: int, stream=None) -> None:
+    """qsa_compress then qsa_index_topk in one scan (appends of at most 5 tokens per request)."""
+    _dt(new_keys, torch.int8); _dt(ring, torch.int8); _dt(ckey_cache, torch.int8); _dt(q_index, torch.int8)
+    _dt(new_cu, torch.int32); _dt(seq_len_before, torch.int32); _dt(block_table, torch.int32)
+    _dt(sel_req, torch.int32); _dt(sel_seq_len, torch.int32); _dt(topk, torch.int32)
+    c = cfg.to_c()
+    B = seq_len_before.shape[0]
+    S = sel_req.shape[0]
+    _check(_lib.load().qsa_compress_index_topk(
+        ctypes.byref(c), B, int(max_new_tokens), _ptr(new_keys), _ptr(new_cu), _ptr(seq_len_before), _ptr(ring),
+        S, int(max_seq_len), _ptr(q_index), _ptr(sel_req), _ptr(sel_seq_len), _ptr(block_table),
+        _ptr(ckey_cache), _ptr(topk), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
 
 
 def qsa_prefill_index_topk(cfg: QSAConfig, q_index: torch.Tensor, row_cu: torch.Tensor,

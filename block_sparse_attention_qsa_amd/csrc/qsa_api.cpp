@@ -136,6 +136,58 @@ qsa_status qsa_index_topk(const qsa_config* cfg, int32_t num_sel_rows, int32_t m
                            block_table, ckey_cache, topk, lay, workspace, stream);
 }
 
+qsa_status qsa_compress_index_topk(const qsa_config* cfg, int32_t num_reqs, int32_t max_new_tokens,
+                                   const int8_t* new_keys, const int32_t* new_cu,
+                                   const int32_t* seq_len_before, int8_t* ring,
+                                   int32_t num_sel_rows, int32_t max_seq_len,
+                                   const int8_t* q_index, const int32_t* sel_req,
+                                   const int32_t* sel_seq_len, const int32_t* block_table,
+                                   int8_t* ckey_cache, int32_t* topk,
+                                   void* workspace, size_t ws_bytes, hipStream_t stream) {
+  qsa_status st = check_config(cfg, true, false);
+  if (st != QSA_OK) return st;
+  if (num_reqs < 0 || num_reqs > 65535)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "num_reqs must be in [0, 65535] (got %d)", num_reqs);
+  if (max_new_tokens < 0 || max_new_tokens > 5)
+    return fail(QSA_ERR_INVALID_ARGUMENT,
+                "qsa_compress_index_topk: max_new_tokens must be in [0, 5] (got %d); use qsa_compress and "
+                "qsa_index_topk for longer appends", max_new_tokens);
+  if (num_sel_rows < 0 || num_sel_rows > 65535)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "num_sel_rows must be in [0, 65535] (got %d)", num_sel_rows);
+  if (max_seq_len < 0 || max_seq_len > QSA_MAX_SEQ_LEN)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "max_seq_len must be in [0, %d] (got %d)", QSA_MAX_SEQ_LEN, max_seq_len);
+  if (num_reqs == 0 && num_sel_rows == 0) return QSA_OK;
+  if (!block_table || !ckey_cache)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_compress_index_topk: NULL array argument");
+  if (num_reqs > 0) {
+    if (!new_cu || !seq_len_before || !ring)
+      return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_compress_index_topk: NULL append argument");
+    if (!new_keys && max_new_tokens > 0)
+      return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_compress_index_topk: new_keys is NULL");
+    if (!aligned(ring, 4) || (new_keys && !aligned(new_keys, 4)))
+      return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_compress_index_topk: ring and new_keys need 4-byte alignment");
+  }
+  if (!aligned(ckey_cache, 16))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_compress_index_topk: ckey_cache needs 16-byte alignment");
+  if (num_sel_rows > 0) {
+    if (!q_index || !sel_req || !sel_seq_len)
+      return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_compress_index_topk: NULL selection argument");
+    if (!aligned(q_index, 4))
+      return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_compress_index_topk: q_index needs 4-byte alignment");
+  }
+  TopkWorkspace lay = topk_workspace_layout(num_sel_rows, max_seq_len);
+  if (num_sel_rows > 0) {
+    if (!workspace) return fail(QSA_ERR_WORKSPACE, "qsa_compress_index_topk: workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(QSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < lay.total)
+      return fail(QSA_ERR_WORKSPACE, "qsa_compress_index_topk: workspace has %zu bytes, needs %zu", ws_bytes,
+                  lay.total);
+  }
+  return launch_compress_index_topk(*cfg, num_reqs, new_keys, new_cu, seq_len_before, ring, ckey_cache,
+                                    num_sel_rows, max_seq_len, q_index, sel_req, sel_seq_len, block_table, topk,
+                                    lay, workspace, stream);
+}
+
 qsa_status qsa_prefill_index_topk(const qsa_config* cfg, int32_t num_reqs, int32_t num_rows,
                                   int32_t max_rows_per_req, int32_t max_seq_len,
                                   const int8_t* q_index, const int32_t* row_cu,

@@ -28,6 +28,7 @@
 //            is emitted in ascending order with a popcount prefix sum and
 //            padded with -1.  It clears the row's histogram, so the workspace
 //            stays clean between calls.
+#include "qsa_append.h"
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -48,6 +49,18 @@ struct WsPtrs {
   uint32_t* hist;
   uint32_t* cinfo;
   int32_t nb_stride;
+};
+
+// The append half of qsa_compress_index_topk (unused by the plain scan).
+struct AppendArgs {
+  const int8_t* new_keys;
+  const int32_t* new_cu;
+  const int32_t* seq_len_before;
+  int8_t* ring;
+  int8_t* ckey;        // the cache the scan reads, written here
+  int32_t num_reqs;
+  int32_t num_rows;    // selecting rows: grid rows below it score
+  int32_t chunks;      // grid columns; grid rows from num_rows on append, one request per workgroup
 };
 
 __device__ __forceinline__ int score_bin(int32_t s) {
@@ -186,24 +199,50 @@ __device__ __forceinline__ void note_max_bin(const int32_t (&sc)[IT], int c, int
   if (lane_id() == 0) atomicMax(s_maxbin, mb);
 }
 
-template <int D>
+// With kAppend (qsa_compress_index_topk) the grid has extra rows after the
+// selecting rows: each of their workgroups appends one request's new tokens
+// (closes its blocks into the cache and writes its ring, as qsa_compress
+// does), while the workgroups above score.  A block closed in this call is scored from its raw keys
+// (the sum over its 4 tokens of q . k is the same integer as q . C), so the
+// scan never depends on the concurrent cache writes: its loads of those blocks
+// are dropped.  The raw keys are the new tokens and, for the block straddling
+// the previous call, ring slots of tokens before seq_len_before; the append
+// writes only the slots of the new tokens, which differ from those while a
+// request gets at most 8 - seq_len_before % 4 tokens (at most 5 always fits,
+// and closes at most 2 blocks).  The raw loads go out with the cache loads, so
+// the closing blocks add no round trip to the workgroups that hold them.
+template <int D, bool kAppend>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     const int8_t* __restrict__ q_index, const int32_t* __restrict__ sel_req,
     const int32_t* __restrict__ sel_seq_len, const int32_t* __restrict__ block_table,
     int32_t max_pages, int32_t page_log2, const int8_t* ckey,
-    int32_t max_seq_len, WsPtrs ws) {
+    int32_t max_seq_len, WsPtrs ws, AppendArgs ap) {
   constexpr int kSChunks = D / 16;       // 16-byte chunks of the s plane
   constexpr int kMaskWords = D / 32;     // dwords per D-bit mask
   constexpr int kMaskLoads = (2 * kMaskWords + 3) / 4;
   __shared__ uint32_t hist[kBins];
   const int s = blockIdx.y;
   const int c = blockIdx.x;
-  const int Lr = sel_seq_len[s];
-  const int b = sel_req[s];
+  // (append variant: grid rows past the selecting rows read the last row's
+  // entries, unused; num_rows >= 1 whenever it runs)
+  const int sr = kAppend ? min(s, ap.num_rows - 1) : s;
+  const int Lr = sel_seq_len[sr];
+  const int b = sel_req[sr];
   // Both row loads and the argument pointers in flight together: the compiler
-  // would otherwise fetch each only after the exit test below, one wait each.
+  // would otherwise fetch each only after the exit tests below, one wait each.
   asm volatile("" ::"s"(Lr), "s"(b), "s"(block_table), "s"(q_index), "s"(ckey), "s"(max_pages),
                "s"(page_log2), "s"(ws.scores), "s"(ws.hist), "s"(ws.nb_stride));
+  if (kAppend) {
+    asm volatile("" ::"s"(ap.seq_len_before), "s"(ap.new_cu), "s"(ap.new_keys), "s"(ap.ring), "s"(ap.num_reqs),
+                 "s"(ap.chunks), "s"(max_seq_len));
+    if (s >= ap.num_rows) {
+      const int r = (s - ap.num_rows) * ap.chunks + c;
+      if (r < ap.num_reqs)
+        append_request<D, kScoreThreads>(r, 0, 1, ap.new_keys, ap.new_cu, ap.seq_len_before, block_table,
+                                         max_pages, page_log2, ap.ring, ap.ckey);
+      return;
+    }
+  }
   const int L = min(Lr, max_seq_len);
   const int nb = max(L, 0) >> 2;
   const int nchunks = (nb + kScoreChunk - 1) / kScoreChunk;
@@ -221,6 +260,20 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   for (int it = 0; it < kScoreIters; ++it) {
     const int j = min(c * kScoreChunk + it * kScoreThreads + (int)threadIdx.x, nb - 1);
     page[it] = bt[j >> bpp_log2];
+  }
+  // This row's request appends after L0 tokens; blocks [jA, jA + nclose) close
+  // in this call (nclose <= 2 for appends of at most 5 tokens).  The loads are
+  // unconditional (num_reqs >= 1 whenever the append variant runs) and issued
+  // after the page-table loads: the exit test above waits for every scalar load
+  // in flight.
+  int L0 = 0, row0 = 0, jA = 0, nclose = 0;
+  if (kAppend) {
+    const int bb = min(max(b, 0), ap.num_reqs - 1);
+    L0 = ap.seq_len_before[bb];
+    row0 = ap.new_cu[bb];
+    const int n = ap.new_cu[bb + 1] - row0;
+    jA = L0 >> 2;
+    nclose = (b == bb && L0 >= 0 && n > 0) ? min(((L0 + n) >> 2) - jA, 2) : 0;
   }
 
   // All key loads at once (non-temporal: streamed once); each block is scored
@@ -243,6 +296,28 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     } else {  // D = 32: 8 mask bytes
       const i32x2 m2 = __builtin_nontemporal_load(reinterpret_cast<const i32x2*>(mp));
       mk[it][0] = i32x4{m2[0], m2[1], 0, 0};
+    }
+  }
+  // Append variant: the raw-key scores of the (up to) two closing blocks, from
+  // dword loads issued beside the cache loads.  Dword w = lane + 64 i of the
+  // pair is block w / D, token (w % D) / (D/4), dims 4 (w % (D/4)) .. +3; every
+  // wave computes both sums itself.  Dwords of blocks that do not close read
+  // the query instead (valid memory; their sum is not used).
+  constexpr int kRawPerLane = D / 32;     // 2 blocks x D dwords / 64 lanes
+  int32_t raw[kRawPerLane], qd[kRawPerLane];
+  if (kAppend) {
+    const int lane = threadIdx.x & 63;
+    const int8_t* qrow = q_index + (size_t)s * D;
+#pragma unroll
+    for (int i = 0; i < kRawPerLane; ++i) {
+      const int w = lane + 64 * i;
+      const int blk = w / D, e = (w % D) / (D / 4), g = w % (D / 4);
+      const int t = kRatio * (jA + blk) + e;
+      const int8_t* src = blk >= nclose ? qrow
+                          : (t >= L0 ? ap.new_keys + (size_t)(row0 + (t - L0)) * D
+                                     : ap.ring + ((size_t)b * kRing + (t & (kRing - 1))) * D);
+      raw[i] = *reinterpret_cast<const int32_t*>(src + 4 * g);
+      qd[i] = *reinterpret_cast<const int32_t*>(qrow + 4 * g);
     }
   }
   // Indexer query: D int8 as D/4 packed dwords (uniform across the workgroup),
@@ -295,6 +370,26 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
       hq += (t == 7) ? -(xt << 7) : (xt << t);
     }
     sc[it] = 256 * hq + sd - 384 * qsum;
+  }
+  if (kAppend) {
+    int32_t p0 = 0, p1 = 0;
+#pragma unroll
+    for (int i = 0; i < kRawPerLane; ++i) {
+      const int32_t p = __builtin_amdgcn_sdot4(raw[i], qd[i], 0, false);
+      const bool first = (lane + 64 * i) < D;
+      p0 += first ? p : 0;
+      p1 += first ? 0 : p;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      p0 += __shfl_xor(p0, o, 64);
+      p1 += __shfl_xor(p1, o, 64);
+    }
+#pragma unroll
+    for (int it = 0; it < kScoreIters; ++it) {
+      const int rel = c * kScoreChunk + it * kScoreThreads + (int)threadIdx.x - jA;
+      sc[it] = (rel >= 0 && rel < nclose) ? (rel == 0 ? p0 : p1) : sc[it];
+    }
   }
   __syncthreads();  // histogram cleared (no key load is outstanding by now)
 #pragma unroll
@@ -729,12 +824,9 @@ qsa_status launch_ws_clear(void* ws, size_t bytes, hipStream_t stream) {
   return check_launch("qsa_index_topk_workspace_init");
 }
 
-qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len,
-                             const int8_t* q_index, const int32_t* sel_req,
-                             const int32_t* sel_seq_len, const int32_t* block_table,
-                             const int8_t* ckey, int32_t* topk, const TopkWorkspace& lay,
-                             void* ws_base, hipStream_t stream) {
-  if (S == 0) return QSA_OK;
+namespace {
+
+WsPtrs ws_ptrs(const TopkWorkspace& lay, void* ws_base) {
   char* base = reinterpret_cast<char*>(ws_base);
   WsPtrs ws;
   ws.scores = reinterpret_cast<int32_t*>(base + lay.off_scores);
@@ -744,30 +836,86 @@ qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len
   ws.hist = reinterpret_cast<uint32_t*>(base + lay.off_hist);
   ws.cinfo = reinterpret_cast<uint32_t*>(base + lay.off_cinfo);
   ws.nb_stride = lay.nb_stride;
+  return ws;
+}
+
+template <bool kAppend>
+qsa_status launch_scan(const qsa_config& c, dim3 grid, const int8_t* q_index, const int32_t* sel_req,
+                       const int32_t* sel_seq_len, const int32_t* block_table, const int8_t* ckey,
+                       int32_t max_seq_len, const WsPtrs& ws, const AppendArgs& ap, hipStream_t stream) {
   const int page_log2 = __builtin_ctz((unsigned)c.page_size);
-  const int chunks = lay.nb_stride / kScoreChunk;
-  dim3 grid(chunks, S);
   switch (c.index_dim) {
     case 32:
-      hipLaunchKernelGGL(score_kernel<32>, grid, dim3(kScoreThreads), 0, stream, q_index, sel_req,
-                         sel_seq_len, block_table, c.max_pages_per_req, page_log2, ckey, max_seq_len, ws);
+      hipLaunchKernelGGL((score_kernel<32, kAppend>), grid, dim3(kScoreThreads), 0, stream, q_index, sel_req,
+                         sel_seq_len, block_table, c.max_pages_per_req, page_log2, ckey, max_seq_len, ws, ap);
       break;
     case 64:
-      hipLaunchKernelGGL(score_kernel<64>, grid, dim3(kScoreThreads), 0, stream, q_index, sel_req,
-                         sel_seq_len, block_table, c.max_pages_per_req, page_log2, ckey, max_seq_len, ws);
+      hipLaunchKernelGGL((score_kernel<64, kAppend>), grid, dim3(kScoreThreads), 0, stream, q_index, sel_req,
+                         sel_seq_len, block_table, c.max_pages_per_req, page_log2, ckey, max_seq_len, ws, ap);
       break;
     case 128:
-      hipLaunchKernelGGL(score_kernel<128>, grid, dim3(kScoreThreads), 0, stream, q_index, sel_req,
-                         sel_seq_len, block_table, c.max_pages_per_req, page_log2, ckey, max_seq_len, ws);
+      hipLaunchKernelGGL((score_kernel<128, kAppend>), grid, dim3(kScoreThreads), 0, stream, q_index, sel_req,
+                         sel_seq_len, block_table, c.max_pages_per_req, page_log2, ckey, max_seq_len, ws, ap);
       break;
     default:
       return fail(QSA_ERR_UNSUPPORTED, "index_dim %d not built", c.index_dim);
   }
-  qsa_status st = check_launch("qsa_index_topk(score)");
+  return QSA_OK;
+}
+
+}  // namespace
+
+qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len,
+                             const int8_t* q_index, const int32_t* sel_req,
+                             const int32_t* sel_seq_len, const int32_t* block_table,
+                             const int8_t* ckey, int32_t* topk, const TopkWorkspace& lay,
+                             void* ws_base, hipStream_t stream) {
+  if (S == 0) return QSA_OK;
+  const WsPtrs ws = ws_ptrs(lay, ws_base);
+  const AppendArgs none{};
+  qsa_status st = launch_scan<false>(c, dim3(lay.nb_stride / kScoreChunk, S), q_index, sel_req, sel_seq_len,
+                                     block_table, ckey, max_seq_len, ws, none, stream);
+  if (st != QSA_OK) return st;
+  st = check_launch("qsa_index_topk(score)");
   if (st != QSA_OK || topk == nullptr) return st;
   hipLaunchKernelGGL(finalize_kernel, dim3(S), dim3(kFinThreads), 0, stream, sel_seq_len, c.topk_blocks,
                      max_seq_len, topk, ws);
   return check_launch("qsa_index_topk(finalize)");
+}
+
+qsa_status launch_compress_index_topk(const qsa_config& c, int32_t num_reqs, const int8_t* new_keys,
+                                      const int32_t* new_cu, const int32_t* seq_len_before, int8_t* ring,
+                                      int8_t* ckey, int32_t S, int32_t max_seq_len, const int8_t* q_index,
+                                      const int32_t* sel_req, const int32_t* sel_seq_len,
+                                      const int32_t* block_table, int32_t* topk, const TopkWorkspace& lay,
+                                      void* ws_base, hipStream_t stream) {
+  if (S == 0 && num_reqs == 0) return QSA_OK;
+  // nothing to select, or nothing to append: the plain calls
+  if (S == 0) return launch_compress(c, num_reqs, 5, new_keys, new_cu, seq_len_before, block_table, ring, ckey, stream);
+  if (num_reqs == 0)
+    return launch_index_topk(c, S, max_seq_len, q_index, sel_req, sel_seq_len, block_table, ckey, topk, lay,
+                             ws_base, stream);
+  const WsPtrs ws = ws_ptrs(lay, ws_base);
+  const int chunks = lay.nb_stride / kScoreChunk;
+  const AppendArgs ap{new_keys, new_cu, seq_len_before, ring, ckey, num_reqs, S, chunks};
+  // the append workgroups come after all scoring ones, so that they do not
+  // change how the scoring workgroups spread over the compute units
+  const int rows = S + (num_reqs + chunks - 1) / chunks;
+  if (rows > 65535) {  // beyond the grid's row limit: the two calls, one after the other
+    qsa_status st = launch_compress(c, num_reqs, 5, new_keys, new_cu, seq_len_before, block_table, ring, ckey,
+                                    stream);
+    if (st != QSA_OK) return st;
+    return launch_index_topk(c, S, max_seq_len, q_index, sel_req, sel_seq_len, block_table, ckey, topk, lay,
+                             ws_base, stream);
+  }
+  qsa_status st = launch_scan<true>(c, dim3(chunks, rows), q_index, sel_req, sel_seq_len,
+                                    block_table, ckey, max_seq_len, ws, ap, stream);
+  if (st != QSA_OK) return st;
+  st = check_launch("qsa_compress_index_topk(append+score)");
+  if (st != QSA_OK || topk == nullptr) return st;
+  hipLaunchKernelGGL(finalize_kernel, dim3(S), dim3(kFinThreads), 0, stream, sel_seq_len, c.topk_blocks,
+                     max_seq_len, topk, ws);
+  return check_launch("qsa_compress_index_topk(finalize)");
 }
 
 qsa_status launch_prefill_index_topk(const qsa_config& c, int32_t B, int32_t R, int32_t max_rows,
@@ -776,15 +924,7 @@ qsa_status launch_prefill_index_topk(const qsa_config& c, int32_t B, int32_t R, 
                                      const int8_t* ckey, int32_t* topk, const TopkWorkspace& lay,
                                      void* ws_base, hipStream_t stream) {
   if (R == 0 || B == 0) return QSA_OK;
-  char* base = reinterpret_cast<char*>(ws_base);
-  WsPtrs ws;
-  ws.scores = reinterpret_cast<int32_t*>(base + lay.off_scores);
-  ws.keys = reinterpret_cast<uint64_t*>(base + lay.off_keys);
-  ws.bitmap = reinterpret_cast<uint64_t*>(base + lay.off_bitmap);
-  ws.keys2 = reinterpret_cast<uint64_t*>(base + lay.off_keys2);
-  ws.hist = reinterpret_cast<uint32_t*>(base + lay.off_hist);
-  ws.cinfo = reinterpret_cast<uint32_t*>(base + lay.off_cinfo);
-  ws.nb_stride = lay.nb_stride;
+  const WsPtrs ws = ws_ptrs(lay, ws_base);
   const int page_log2 = __builtin_ctz((unsigned)c.page_size);
   const int chunks = lay.nb_stride / kScoreChunk;
   dim3 grid(chunks, (max_rows + kPfRows - 1) / kPfRows, B);

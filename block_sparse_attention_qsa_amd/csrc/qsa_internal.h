@@ -45,6 +45,12 @@ qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len
                              const int8_t* ckey, int32_t* topk, const TopkWorkspace& ws,
                              void* ws_base, hipStream_t stream);
 
+qsa_status launch_compress_index_topk(const qsa_config& c, int32_t num_reqs, const int8_t* new_keys,
+                                      const int32_t* new_cu, const int32_t* seq_len_before, int8_t* ring,
+                                      int8_t* ckey, int32_t S, int32_t max_seq_len, const int8_t* q_index,
+                                      const int32_t* sel_req, const int32_t* sel_seq_len,
+                                      const int32_t* block_table, int32_t* topk, const TopkWorkspace& lay,
+                                      void* ws_base, hipStream_t stream);
 qsa_status launch_prefill_index_topk(const qsa_config& c, int32_t B, int32_t R, int32_t max_rows,
                                      int32_t max_seq_len, const int8_t* q_index, const int32_t* row_cu,
                                      const int32_t* row_seq_len, const int32_t* block_table,

@@ -5,7 +5,9 @@ top-k workspace, selection, split partials, output) for a Workload, and runs
 
     compress  ->  index_topk  ->  sparse_decode  ->  merge_partials
 
-on one stream.  It only allocates and sequences; all arithmetic is in libqsa.so.
+on one stream; when the step appends at most 5 tokens per request the first
+two are one call, qsa_compress_index_topk (fuse_append=False keeps them apart).
+It only allocates and sequences; all arithmetic is in libqsa.so.
 """
 from __future__ import annotations
 
@@ -43,7 +45,8 @@ def _rows(keys: torch.Tensor, key_off: np.ndarray, lo: np.ndarray, hi: np.ndarra
 
 class QSALayer:
     def __init__(self, wl: Workload, num_splits: int = 1, poison: bool = False,
-                 max_seq_len: Optional[int] = None, out_dtype: torch.dtype = torch.float32):
+                 max_seq_len: Optional[int] = None, out_dtype: torch.dtype = torch.float32,
+                 fuse_append: bool = True):
         dev = wl.q.device
         self.wl = wl
         self.cfg = config_for(wl)
@@ -70,6 +73,7 @@ class QSALayer:
         self.step_cu = torch.as_tensor(cu.astype(np.int32), device=dev)
         self.step_before = torch.as_tensor(wl.prefix_len.astype(np.int32), device=dev)
         self.step_max_new = int((wl.final_len - wl.prefix_len).max()) if B else 0
+        self.fused = bool(fuse_append) and self.step_max_new <= 5
 
     def prefill(self, chunk: Optional[int] = None) -> None:
         """Bulk-compress every request's prefix [0, prefix_len) (optionally in chunks)."""
@@ -95,6 +99,12 @@ class QSALayer:
         api.qsa_index_topk(self.cfg, wl.q_index, wl.sel_req, wl.sel_seq_len, wl.block_table, self.ckey,
                            self.topk, self.workspace, self.max_seq_len, stream=stream)
 
+    def compress_index(self, stream=None) -> None:
+        wl = self.wl
+        api.qsa_compress_index_topk(self.cfg, self.step_keys, self.step_cu, self.step_before, self.ring,
+                                    wl.q_index, wl.sel_req, wl.sel_seq_len, wl.block_table, self.ckey, self.topk,
+                                    self.workspace, self.step_max_new, self.max_seq_len, stream=stream)
+
     def decode(self, stream=None) -> None:
         wl = self.wl
         api.qsa_sparse_decode(self.cfg, wl.q, wl.row_seq_len, wl.sel_req, wl.sel_seq_len, self.topk,
@@ -106,8 +116,11 @@ class QSALayer:
 
     def step(self, stream=None) -> None:
         """One decode step: the whole hot path."""
-        self.compress(stream)
-        self.index(stream)
+        if self.fused:
+            self.compress_index(stream)
+        else:
+            self.compress(stream)
+            self.index(stream)
         self.decode(stream)
         self.merge(stream)
 
@@ -119,7 +132,8 @@ class QSAPrefill(QSALayer):
 
     def __init__(self, wl: Workload, num_splits: int = 1, poison: bool = False,
                  max_seq_len: Optional[int] = None, out_dtype: torch.dtype = torch.float32):
-        super().__init__(wl, num_splits=num_splits, poison=poison, max_seq_len=max_seq_len, out_dtype=out_dtype)
+        super().__init__(wl, num_splits=num_splits, poison=poison, max_seq_len=max_seq_len, out_dtype=out_dtype,
+                         fuse_append=False)
         self.row_cu = wl.extra["row_cu"]
         self.max_rows = int(wl.extra["max_rows_per_req"])
 

@@ -174,6 +174,41 @@ qsa_status qsa_index_topk(const qsa_config* cfg, int32_t num_sel_rows, int32_t m
                           void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * qsa_compress_index_topk -- qsa_compress followed by qsa_index_topk, in one
+ * scan launch (plus the selection), for decode-sized appends.  [QSA-DCP]: each
+ * decode step appends the new tokens' keys to the compressed side cache and
+ * the indexer then keeps the best 512 blocks; [PR53896]: ring, pooling into
+ * the compressed cache, weight-free top-k with -1 padding.
+ *
+ * The arguments are those of the two calls (cfg and block_table are shared):
+ * request b < num_reqs appends rows [new_cu[b], new_cu[b+1]) of new_keys after
+ * seq_len_before[b] tokens, and selecting row s < num_sel_rows (request
+ * sel_req[s], context sel_seq_len[s]) is scored over the cache as it stands
+ * after the append.  ring, ckey_cache, topk and the workspace end exactly as
+ * after qsa_compress(...) then qsa_index_topk(...) on the same stream, bit for
+ * bit; the rollback rule of qsa_compress holds unchanged.
+ *   max_new_tokens: 0..5, a bound on every request's new token count (that
+ *                   many tokens never overwrite the ring slots that the scan
+ *                   reads for the block straddling seq_len_before[b]).  A
+ *                   request with more new tokens than that is undefined.
+ *   sel_req[s] outside [0, num_reqs) reads the cache as it stands (no tokens
+ *                   of this call).
+ *   new_keys, ring: 4-byte aligned; topk == NULL scores only, as in
+ *                   qsa_index_topk.  num_sel_rows = 0 only appends (as
+ *                   qsa_compress), num_reqs = 0 only selects.
+ * Errors: INVALID_ARGUMENT (as either call, or max_new_tokens > 5),
+ *         UNSUPPORTED (index_dim), WORKSPACE, HIP.
+ */
+qsa_status qsa_compress_index_topk(const qsa_config* cfg, int32_t num_reqs, int32_t max_new_tokens,
+                                   const int8_t* new_keys, const int32_t* new_cu,
+                                   const int32_t* seq_len_before, int8_t* ring,
+                                   int32_t num_sel_rows, int32_t max_seq_len,
+                                   const int8_t* q_index, const int32_t* sel_req,
+                                   const int32_t* sel_seq_len, const int32_t* block_table,
+                                   int8_t* ckey_cache, int32_t* topk,
+                                   void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * qsa_prefill_index_topk -- qsa_index_topk for a chunk of prefill query rows:
  * many rows per request, each with its own causal length (sparse / chunked
  * prefill; [QSA-DCP], section on why the pull request matters, names a native

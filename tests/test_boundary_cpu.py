@@ -183,3 +183,25 @@ def test_indexer_project_rejects(lib):
     assert fe(q=ctypes.c_void_p(0x10002)) == 1
     assert fe(T=0) == 0
 
+
+
+def test_compress_index_topk_rejects(lib):
+    c = cfg()
+    n = lib.qsa_index_topk_workspace_size(ctypes.byref(c), 8, 65536)
+
+    def ci(B=4, mx=1, S=8, L=65536, keys=FAKE, ring=FAKE, q=FAKE, ws=FAKE, nbytes=n, **kw):
+        return lib.qsa_compress_index_topk(ctypes.byref(kw.get("c", c)), B, mx, keys, FAKE, FAKE, ring, S, L, q,
+                                           FAKE, FAKE, FAKE, FAKE, FAKE, ws, nbytes, None)
+    assert ci(mx=6) == 1                              # longer appends: the two separate calls
+    assert ci(mx=-1) == 1
+    assert ci(B=-1) == 1
+    assert ci(S=-1) == 1
+    assert ci(L=_lib.QSA_MAX_SEQ_LEN + 4) == 1
+    assert ci(keys=None) == 1
+    assert ci(ring=ctypes.c_void_p(0x10002)) == 1     # ring not 4-byte aligned
+    assert ci(keys=ctypes.c_void_p(0x10001)) == 1
+    assert ci(q=None) == 1
+    assert ci(nbytes=n - 1) == 3
+    assert ci(ws=None) == 3
+    assert ci(c=cfg(index_dim=96)) == 2
+    assert ci(B=0, S=0) == 0
