@@ -168,16 +168,26 @@ __device__ __forceinline__ void chunk_candidates(const uint32_t* hist, int maxbi
   }
   __syncthreads();
   const int lb = *s_lb;
+  // one slot reservation per wave for all its iterations
+  bool take[IT];
+  uint64_t mask[IT];
+  uint32_t total = 0;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int j = c * kScoreChunk + it * NT + tid;
-    const bool take = j < nb && score_bin(sc[it]) >= lb;
-    const uint64_t mask = __ballot(take);
-    if (mask) {
-      uint32_t base = 0;
-      if (l == 0) base = atomicAdd(s_cnt, (uint32_t)__popcll(mask));
-      base = __shfl(base, 0, 64);
-      if (take) keys[base + (uint32_t)__popcll(mask & ((1ull << l) - 1ull))] = cand_key(sc[it], (uint32_t)j);
+    take[it] = j < nb && score_bin(sc[it]) >= lb;
+    mask[it] = __ballot(take[it]);
+    total += (uint32_t)__popcll(mask[it]);
+  }
+  if (total) {
+    uint32_t base = 0;
+    if (l == 0) base = atomicAdd(s_cnt, total);
+    base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int j = c * kScoreChunk + it * NT + tid;
+      if (take[it]) keys[base + lanes_below(mask[it])] = cand_key(sc[it], (uint32_t)j);
+      base += (uint32_t)__popcll(mask[it]);
     }
   }
   __syncthreads();
@@ -194,8 +204,7 @@ __device__ __forceinline__ void note_max_bin(const int32_t (&sc)[IT], int c, int
     const int j = c * kScoreChunk + it * nt + (int)threadIdx.x;
     mb = max(mb, j < nb ? score_bin(sc[it]) : -1);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mb = max(mb, __shfl_xor(mb, o, 64));
+  mb = wave_max_i32(mb);
   if (lane_id() == 0) atomicMax(s_maxbin, mb);
 }
 
@@ -344,9 +353,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
       if (2 * h + 1 < kMaskWords) qp[t][2 * h + 1] = (uint32_t)(m >> 32);
     }
   }
+  // The histogram is cleared while the keys stream in (a barrier does not wait
+  // for outstanding loads), so the arithmetic below is followed by no barrier
+  // before the histogram updates.
   __shared__ int s_maxbin;
   for (int i = threadIdx.x; i < kBins; i += kScoreThreads) hist[i] = 0;
   if (threadIdx.x == 0) s_maxbin = -1;
+  __syncthreads();
   int32_t sc[kScoreIters];
 #pragma unroll
   for (int it = 0; it < kScoreIters; ++it) {
@@ -380,18 +393,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
       p0 += first ? p : 0;
       p1 += first ? 0 : p;
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      p0 += __shfl_xor(p0, o, 64);
-      p1 += __shfl_xor(p1, o, 64);
-    }
+    p0 = (int32_t)__builtin_amdgcn_readlane((int)wave_incl_scan((uint32_t)p0), 63);
+    p1 = (int32_t)__builtin_amdgcn_readlane((int)wave_incl_scan((uint32_t)p1), 63);
 #pragma unroll
     for (int it = 0; it < kScoreIters; ++it) {
       const int rel = c * kScoreChunk + it * kScoreThreads + (int)threadIdx.x - jA;
       sc[it] = (rel >= 0 && rel < nclose) ? (rel == 0 ? p0 : p1) : sc[it];
     }
   }
-  __syncthreads();  // histogram cleared (no key load is outstanding by now)
 #pragma unroll
   for (int it = 0; it < kScoreIters; ++it) {
     const int j = c * kScoreChunk + it * kScoreThreads + threadIdx.x;
