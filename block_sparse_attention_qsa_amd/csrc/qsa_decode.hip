@@ -125,30 +125,49 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int l = lane_id(), w = threadIdx.x / 64;
   const int lc = l & 15, lg = l >> 4;
 
+  // The split's block ids for a row with at least k closed blocks (nsel = k,
+  // the usual case at long context), loaded before the row's length is known:
+  // one dependent round trip less.  Used when the row turns out to be that long
+  // and the split fits the workgroup; otherwise they are loaded again below.
+  // (p * k <= 64 * 2048: 32-bit products and quotients)
+  const int lo_full = (p * a.k) / a.P;
+  const int n_full = ((p + 1) * a.k) / a.P - lo_full;
+  const int spec_blk = a.topk[(size_t)s * a.k + lo_full + min((int)threadIdx.x, max(n_full - 1, 0))];
+
   const int b = a.sel_req[s];
   const int Lsel = max(a.sel_seq_len[s], 0);
-  int tail_hi = 0;
-  for (int i = 0; i < a.qps; ++i) tail_hi = max(tail_hi, a.row_seq_len[s * a.qps + i]);
-  // Q as the QK MFMA B operand: lane (lc, lg) holds head n = nt*16+lc, dims 32kk+8lg..+8.
+  // Q as the QK MFMA B operand: lane (lc, lg) holds head n = nt*16+lc, dims
+  // 32kk+8lg..+8.  The loads are unconditional (padding heads read the group's
+  // first head and are zeroed), so they all go out with the loads above.
   bf16x8 bq[NT][KK];
   int rlen[NT];  // context length of the row owning head nt*16+lc
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int n = nt * 16 + lc;
     const bool real = n < a.nh;
-    const int i = real ? n / a.G : 0;
-    const int h = kvh * a.G + (real ? n % a.G : 0);
+    const int nn = real ? n : 0;
+    const int i = nn / a.G;
+    const int h = kvh * a.G + (nn - i * a.G);
     const uint16_t* qrow = a.q + ((size_t)(s * a.qps + i) * a.Hq + h) * D;
-    rlen[nt] = real ? a.row_seq_len[s * a.qps + i] : -1;
+    const int rl = a.row_seq_len[s * a.qps + i];
+    rlen[nt] = real ? rl : -1;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      i32x4 v = real ? ld16(qrow + 32 * kk + 8 * lg) : i32x4{0, 0, 0, 0};
-      bq[nt][kk] = __builtin_bit_cast(bf16x8, v);
+      const i32x4 v = ld16(qrow + 32 * kk + 8 * lg);
+      bq[nt][kk] = __builtin_bit_cast(bf16x8, real ? v : i32x4{0, 0, 0, 0});
     }
   }
+  // the request and the selecting row's length, fetched while the vector loads
+  // above are in flight (the compiler would otherwise fetch them at first use)
+  asm volatile("" ::"s"(b), "s"(Lsel));
+  // longest row of the selection: every row owns some head n < nh
+  int tail_hi = 0;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) tail_hi = max(tail_hi, rlen[nt]);
+  tail_hi = wave_max_i32(tail_hi);
   const int nsel = (Lsel >= 4) ? min(a.k, Lsel >> 2) : 0;
-  const int lo = (int)(((int64_t)p * nsel) / a.P);
-  const int hi = (int)(((int64_t)(p + 1) * nsel) / a.P);
+  const int lo = (p * nsel) / a.P;
+  const int hi = ((p + 1) * nsel) / a.P;
   const int nblk = hi - lo;
   const int tail_lo = 4 * (Lsel >> 2);
   const int ntailblk = (p == a.P - 1) ? (max(0, tail_hi - tail_lo) + 3) >> 2 : 0;
@@ -174,6 +193,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     return (((pos >> a.page_log2) * a.Hkv + kvh) << a.page_log2) | (pos & (page_size - 1));
   };
 
+  const bool use_spec = nsel == a.k && n_full <= kThreads;  // then lo == lo_full, nblk == n_full
   for (int r0 = 0; r0 < nall; r0 += kRound) {
     const int nr = min(kRound, nall - r0);
     // ---- stage block ids and page positions of this round in LDS ----
@@ -182,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       const int u = r0 + i;
       int tok = -1, pos = 0;
       if (u < nblk) {
-        const int j = sel[u];
+        const int j = use_spec ? spec_blk : sel[u];  // use_spec: one round, u == threadIdx.x
         tok = (j >= 0) ? 4 * j : -1;
       } else {
         tok = tail_lo + 4 * (u - nblk);
