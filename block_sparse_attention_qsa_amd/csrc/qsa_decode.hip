@@ -19,9 +19,11 @@
 //   * PV:    v_mfma_f32_16x16x16_bf16, M = 16 heads, N = 16 dims, K = 16 slots.
 //            The QK accumulator layout is already the PV A-operand layout, so P
 //            never leaves registers; it is split into two bf16 terms (hi + lo)
-//            to keep ~16 mantissa bits.  V is loaded as dwords (two adjacent
-//            dims) of the four rows each lane group needs and permuted into the
-//            B operand.
+//            to keep ~16 mantissa bits.  The output dims are permuted: column
+//            lc of PV chunk m is dim (D/16) lc + m, so lane lc loads D/16
+//            consecutive dims of each of its four V rows in one load per row
+//            (16 B for bf16 at d = 128) and builds the B operands with byte
+//            permutes; the permutation is undone when the output is written.
 // Block ids and page positions of a split are staged in LDS once; K/V loads
 // run one tile ahead.  Four waves take interleaved tiles and are merged in
 // LDS in a fixed order (deterministic).  FP8 (OCP E4M3) K/V are widened
@@ -78,10 +80,10 @@ constexpr int kRound = 512;  // blocks staged in LDS per round
 template <int D, bool FP8>
 struct TileLoad {
   static constexpr int KK = D / 32;
-  static constexpr int NPAIR = D / 32;  // pairs of 16-wide d-chunks
+  static constexpr int VDW = (D / 16) * (FP8 ? 1 : 2) / 4;  // dwords of one V row slice per lane
   i32x4 k[FP8 ? 1 : KK];   // bf16: 16 B per k-step
   i32x2 k8[FP8 ? KK : 1];  // fp8: 8 B per k-step
-  uint32_t v[NPAIR][4];    // V of slots 4*lg+e at dims 32q+2lc, 32q+2lc+1
+  uint32_t v[4][VDW];      // V of slots 4*lg+e at dims (D/16) lc .. (D/16) lc + D/16 - 1
   int tok;                 // first token of the block of slots 4*lg..4*lg+3 (-1: none)
   f32x4 ks, vs;            // fp8 scales of those four slots
 };
@@ -111,7 +113,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   constexpr int NT = (NH + 15) / 16;  // MFMA tiles of 16 heads
   constexpr int NHP = NT * 16;        // heads padded to whole tiles
   constexpr int KK = D / 32;          // QK MFMA k steps over the head dim
-  constexpr int NPAIR = D / 32;       // PV: pairs of 16-wide d-chunks
+  constexpr int NPAIR = D / 32;       // PV: pairs of 16-wide d-chunks (bf16 dwords of a V slice)
+  constexpr int VDW = TileLoad<D, FP8>::VDW;
   constexpr int NM = D / 16;          // PV MFMAs (16-wide d-chunks) per head tile
 
   __shared__ float ml_lds[kWaves][2][NHP];
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int32_t* sel = a.topk + (size_t)s * a.k + lo;
 
   float m_run[NT], l_run[NT];
-  // O in the MFMA C layout: acc[nt][m][e] = O[head nt*16+4lg+e][d = 32(m/2) + 2lc + m%2]
+  // O in the MFMA C layout: acc[nt][m][e] = O[head nt*16+4lg+e][d = (D/16) lc + m]
   f32x4 acc[NT][NM];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -239,11 +242,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        const size_t el = (size_t)(row_c + (tok_c >= 0 ? e : 0)) * D + (D / 16) * lc;  // element index
+        const char* src = vbase + el * (FP8 ? 1 : 2);
+        if (VDW == 4) {
+          const i32x4 x = ld16(src);
 #pragma unroll
-        for (int q = 0; q < NPAIR; ++q) {
-          const size_t el = (size_t)(row_c + (tok_c >= 0 ? e : 0)) * D + 32 * q + 2 * lc;
-          if (FP8) tl.v[q][e] = *reinterpret_cast<const uint16_t*>(vbase + el);
-          else tl.v[q][e] = *reinterpret_cast<const uint32_t*>(vbase + el * 2);
+          for (int r = 0; r < 4; ++r) tl.v[e][r] = (uint32_t)x[r];
+        } else if (VDW == 2) {
+          const i32x2 x = *reinterpret_cast<const i32x2*>(src);
+          tl.v[e][0] = (uint32_t)x[0];
+          tl.v[e][VDW - 1] = (uint32_t)x[1];
+        } else {
+          tl.v[e][0] = *reinterpret_cast<const uint32_t*>(src);
         }
       }
     };
@@ -270,17 +280,28 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       }
       // V operand (B: K = 16 slots, N = 16 dims): lane (lc, lg) holds slots 4lg..4lg+3
       // of dim 32q + 2lc + h for chunk m = 2q + h.
+      // Chunk m = 2q + h is dim (D/16) lc + m: the low (h = 0) or high bf16 of
+      // dword q of each slot's slice.
       s16x4 bv[NM];
+      uint32_t vb[4][NPAIR];  // bf16 pairs: dims (D/16) lc + 2q, +1 of slot 4lg+e
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (FP8) {  // four e4m3 bytes -> four bf16 (exact): two dwords
+#pragma unroll
+          for (int r = 0; r < VDW; ++r) {
+            auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cur.v[e][r], false);
+            auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cur.v[e][r], true);
+            vb[e][2 * r] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
+            vb[e][2 * r + 1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < NPAIR; ++r) vb[e][r] = cur.v[e][r];
+        }
+      }
 #pragma unroll
       for (int q = 0; q < NPAIR; ++q) {
-        uint32_t w0 = cur.v[q][0], w1 = cur.v[q][1], w2 = cur.v[q][2], w3 = cur.v[q][3];
-        if (FP8) {  // two e4m3 bytes -> two bf16 (exact) per slot
-          auto cv = [](uint32_t x) -> uint32_t {
-            auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, false);
-            return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
-          };
-          w0 = cv(w0); w1 = cv(w1); w2 = cv(w2); w3 = cv(w3);
-        }
+        const uint32_t w0 = vb[0][q], w1 = vb[1][q], w2 = vb[2][q], w3 = vb[3][q];
         bv[2 * q + 0] = pack4(__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u));
         bv[2 * q + 1] = pack4(__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u));
       }
@@ -355,8 +376,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       const int n = nt * 16 + 4 * lg + e;
       if (n < NH) {
 #pragma unroll
-        for (int q = 0; q < NPAIR; ++q)
-          *reinterpret_cast<float2*>(&o_w[w][n][32 * q + 2 * lc]) = float2{acc[nt][2 * q][e], acc[nt][2 * q + 1][e]};
+        for (int m4 = 0; m4 < NM / 4; ++m4)
+          *reinterpret_cast<f32x4*>(&o_w[w][n][(D / 16) * lc + 4 * m4]) =
+              f32x4{acc[nt][4 * m4][e], acc[nt][4 * m4 + 1][e], acc[nt][4 * m4 + 2][e], acc[nt][4 * m4 + 3][e]};
       }
     }
   }
@@ -407,15 +429,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
   const int l = lane_id();
   const int rh = blockIdx.x * 4 + threadIdx.x / 64;
   if (rh >= RH) return;
-  const float lp = (l < P) ? lse_part[(size_t)l * RH + rh] : -INFINITY;
-  float v[CH][DPL];
+  const float lp_raw = lse_part[(size_t)min(l, P - 1) * RH + rh];
+  const float lp = (l < P) ? lp_raw : -INFINITY;
+  typedef float fvec __attribute__((ext_vector_type(DPL)));
+  fvec v[CH];
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const float* src = o_part + ((size_t)min(i, P - 1) * RH + rh) * D + l * DPL;
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) v[i][j] = src[j];
-  }
-  const float M = wave_max(lp);
+  for (int i = 0; i < CH; ++i)
+    v[i] = *reinterpret_cast<const fvec*>(o_part + ((size_t)min(i, P - 1) * RH + rh) * D + l * DPL);
+  const float M = wave_max_dpp(lp);
   float acc[DPL];
 #pragma unroll
   for (int j = 0; j < DPL; ++j) acc[j] = 0.f;
@@ -423,26 +444,24 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
     if (l == 0) lse[rh] = -INFINITY;
   } else {
     const float wgt = (lp == -INFINITY) ? 0.f : expf(lp - M);
-    const float sum = wave_sum(wgt);
+    const float sum = wave_sum_dpp(wgt);
     if (l == 0) lse[rh] = M + logf(sum);
     const float inv = 1.f / sum;
     // empty partials have weight 0 and finite (zero) outputs
+    // lane i's weight, read with readlane (i is uniform)
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const float wp = (i < P) ? __shfl(wgt, i, 64) * inv : 0.f;
+      const float wp = (i < P) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), i)) * inv : 0.f;
 #pragma unroll
       for (int j = 0; j < DPL; ++j) acc[j] = fmaf(wp, v[i][j], acc[j]);
     }
     for (int p0 = CH; p0 < P; p0 += CH) {
 #pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const float* src = o_part + ((size_t)min(p0 + i, P - 1) * RH + rh) * D + l * DPL;
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) v[i][j] = src[j];
-      }
+      for (int i = 0; i < CH; ++i)
+        v[i] = *reinterpret_cast<const fvec*>(o_part + ((size_t)min(p0 + i, P - 1) * RH + rh) * D + l * DPL);
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
-        const float wp = (p0 + i < P) ? __shfl(wgt, p0 + i, 64) * inv : 0.f;
+        const float wp = (p0 + i < P) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), p0 + i)) * inv : 0.f;
 #pragma unroll
         for (int j = 0; j < DPL; ++j) acc[j] = fmaf(wp, v[i][j], acc[j]);
       }

@@ -75,6 +75,28 @@ __device__ __forceinline__ int wave_max_i32(int v) {
              max(__builtin_amdgcn_readlane(v, 47), __builtin_amdgcn_readlane(v, 63)));
 }
 
+// fp32 maximum and sum across the wave, uniform results, by the same DPP row
+// shifts plus readlane of the four row ends (no LDS).  The sum adds in a fixed
+// order (rows, then the four row sums), so it is deterministic.
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  int v = __float_as_int(x);
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x111, 0xf, 0xf, false))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x112, 0xf, 0xf, false))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x114, 0xf, 0xf, false))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x118, 0xf, 0xf, false))));
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(v, 15)), __int_as_float(__builtin_amdgcn_readlane(v, 31))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(v, 47)), __int_as_float(__builtin_amdgcn_readlane(v, 63))));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  int v = __float_as_int(x);
+  v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true)));
+  return (__int_as_float(__builtin_amdgcn_readlane(v, 15)) + __int_as_float(__builtin_amdgcn_readlane(v, 31))) +
+         (__int_as_float(__builtin_amdgcn_readlane(v, 47)) + __int_as_float(__builtin_amdgcn_readlane(v, 63)));
+}
+
 // Round-to-nearest-even fp32 -> bf16 bits (NaN kept quiet).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
