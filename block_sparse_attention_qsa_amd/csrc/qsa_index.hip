@@ -160,7 +160,7 @@ __device__ __forceinline__ void chunk_candidates(const uint32_t* hist, int maxbi
         found = true;
         lb = top - (__ffsll((long long)hit) - 1);
       } else {
-        acc = __shfl(inc, 63, 64);
+        acc = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
         top -= 64;
       }
     }
@@ -616,9 +616,9 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
         acc += cs[i];
       }
       const int src = __ffsll((long long)__ballot(mine)) - 1;
-      dsel = __shfl(dsel, src, 64);
-      larger = __shfl(larger, src, 64);
-      cnt = __shfl(cnt, src, 64);
+      dsel = (uint32_t)__builtin_amdgcn_readlane((int)dsel, src);
+      larger = (uint32_t)__builtin_amdgcn_readlane((int)larger, src);
+      cnt = (uint32_t)__builtin_amdgcn_readlane((int)cnt, src);
       rem -= larger;
       prefix = (prefix & ~(0xffull << shift)) | ((uint64_t)dsel << shift);
       mask |= 0xffull << shift;
