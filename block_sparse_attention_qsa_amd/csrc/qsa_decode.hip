@@ -25,10 +25,10 @@
 //            (16 B for bf16 at d = 128) and builds the B operands with byte
 //            permutes; the permutation is undone when the output is written.
 // Block ids and page positions of a split are staged in LDS once; K/V loads
-// run one tile ahead.  Four waves take interleaved tiles and are merged in
-// LDS in a fixed order (deterministic).  FP8 (OCP E4M3) K/V are widened
-// exactly to bf16; the per-token K scale multiplies the logit and the V scale
-// multiplies the probability.
+// run one tile ahead.  The waves (8, or 4 for large head groups) take
+// interleaved tiles and are merged in LDS in a fixed order (deterministic).
+// FP8 (OCP E4M3) K/V are widened exactly to bf16; the per-token K scale
+// multiplies the logit and the V scale multiplies the probability.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -36,8 +36,10 @@ namespace qsa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+// Waves per workgroup: 8 (one 16-slot tile each for a split of 32 blocks)
+// while the per-wave output staging fits the LDS, else 4.
+template <int D, int NH>
+constexpr int decode_waves() { return NH <= 16 ? 8 : 4; }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -109,7 +111,9 @@ __device__ __forceinline__ float sum_lg(float v) {
 }
 
 template <int D, int NH, bool FP8>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__((decode_waves<D, NH>() * 64)) void decode_kernel(DecodeArgs a) {
+  constexpr int kWaves = decode_waves<D, NH>();
+  constexpr int kThreads = kWaves * 64;
   constexpr int NT = (NH + 15) / 16;  // MFMA tiles of 16 heads
   constexpr int NHP = NT * 16;        // heads padded to whole tiles
   constexpr int KK = D / 32;          // QK MFMA k steps over the head dim
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- merge the four waves (fixed order => deterministic) ----
+  // ---- merge the waves (fixed order => deterministic) ----
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     if (lg == 0) { ml_lds[w][0][nt * 16 + lc] = m_run[nt]; ml_lds[w][1][nt * 16 + lc] = l_run[nt]; }
@@ -476,7 +480,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
 
 template <int D, int NH, bool FP8>
 qsa_status launch_decode_t(dim3 grid, const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, NH, FP8>), grid, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<D, NH, FP8>), grid, dim3(decode_waves<D, NH>() * 64), 0, stream, a);
   return check_launch("qsa_sparse_decode");
 }
 
