@@ -424,14 +424,14 @@ __global__ __launch_bounds__((decode_waves<D, NH>() * 64)) void decode_kernel(De
 // time), then reduced: lane p holds lse_p; the outputs are weighted by
 // exp(lse_p - lse) broadcast from lane p.
 template <int D, typename OutT>
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_part,
+__global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ o_part,
                                                     const float* __restrict__ lse_part,
                                                     OutT* __restrict__ out, float* __restrict__ lse,
                                                     int32_t P, int32_t RH) {
   constexpr int DPL = D / 64;
   constexpr int CH = 16;
   const int l = lane_id();
-  const int rh = blockIdx.x * 4 + threadIdx.x / 64;
+  const int rh = blockIdx.x;
   if (rh >= RH) return;
   const float lp_raw = lse_part[(size_t)min(l, P - 1) * RH + rh];
   const float lp = (l < P) ? lp_raw : -INFINITY;
@@ -541,15 +541,15 @@ qsa_status launch_merge(int32_t P, int32_t R, int32_t H, int32_t d, const float*
                         const float* lse_part, void* out, bool out_bf16, float* lse, hipStream_t stream) {
   const int RH = R * H;
   if (RH == 0) return QSA_OK;
-  dim3 grid((RH + 3) / 4);
+  dim3 grid(RH);  // one wave per (row, head): the loads spread over more CUs
   uint16_t* ob = reinterpret_cast<uint16_t*>(out);
   float* of = reinterpret_cast<float*>(out);
   if (d == 128) {
-    if (out_bf16) hipLaunchKernelGGL((merge_kernel<128, uint16_t>), grid, dim3(256), 0, stream, o_part, lse_part, ob, lse, P, RH);
-    else hipLaunchKernelGGL((merge_kernel<128, float>), grid, dim3(256), 0, stream, o_part, lse_part, of, lse, P, RH);
+    if (out_bf16) hipLaunchKernelGGL((merge_kernel<128, uint16_t>), grid, dim3(64), 0, stream, o_part, lse_part, ob, lse, P, RH);
+    else hipLaunchKernelGGL((merge_kernel<128, float>), grid, dim3(64), 0, stream, o_part, lse_part, of, lse, P, RH);
   } else if (d == 64) {
-    if (out_bf16) hipLaunchKernelGGL((merge_kernel<64, uint16_t>), grid, dim3(256), 0, stream, o_part, lse_part, ob, lse, P, RH);
-    else hipLaunchKernelGGL((merge_kernel<64, float>), grid, dim3(256), 0, stream, o_part, lse_part, of, lse, P, RH);
+    if (out_bf16) hipLaunchKernelGGL((merge_kernel<64, uint16_t>), grid, dim3(64), 0, stream, o_part, lse_part, ob, lse, P, RH);
+    else hipLaunchKernelGGL((merge_kernel<64, float>), grid, dim3(64), 0, stream, o_part, lse_part, of, lse, P, RH);
   } else {
     return fail(QSA_ERR_UNSUPPORTED, "head_dim %d not built", d);
   }
