@@ -532,9 +532,6 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   }
   if (tid == 0) { s_n = 0; s_T = 0; s_above = 0; }
   threshold_from_counts<kFinThreads>(hc, ks, sh, &s_T, &s_above);
-  // the row histogram is consumed: clear it for the next call (each thread the bins it read)
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) ghist[kBins - 1 - (kPer * tid + i)] = 0;
   const int T = s_T;
   const uint32_t above = s_above;
 
@@ -560,19 +557,43 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
 #pragma unroll
       for (int e = 0; e < kFinKeys; ++e) kk[e] = ckeys[(size_t)cc * kScoreChunk + sub * kFinKeys + e];
     }
+    uint32_t at_t = 0;  // which of this thread's first-round keys are threshold candidates
     if (c < nchunks) {
       const uint32_t cnt = ci >> 16;
       const int lb = (int)(ci & 0xffffu);
       if (lb <= T) {  // the list holds every block of this chunk with bin >= T
 #pragma unroll
-        for (int e = 0; e < kFinKeys; ++e)
-          if ((uint32_t)(sub * kFinKeys + e) < cnt) classify(kk[e]);
+        for (int e = 0; e < kFinKeys; ++e) {
+          const int bin = score_bin(key_score(kk[e]));
+          const bool valid = (uint32_t)(sub * kFinKeys + e) < cnt;
+          if (valid && bin > T) mark(0xffffffffu - (uint32_t)(kk[e] & 0xffffffffull));
+          at_t |= (valid && bin == T) ? 1u << e : 0u;
+        }
         for (uint32_t i = (uint32_t)(tpc * kFinKeys + sub); i < cnt; i += tpc)
           classify(ckeys[(size_t)c * kScoreChunk + i]);
       } else {  // local bin above T: blocks of bins [T, lb) are not listed; read the chunk's scores
         for (int i = sub; i < kScoreChunk; i += tpc) {
           const int j = c * kScoreChunk + i;
           if (j < nb) classify(cand_key(srow[j], (uint32_t)j));
+        }
+      }
+    }
+    // The first-round threshold candidates are appended with one slot
+    // reservation per wave (a wave prefix sum of the per-thread counts), so no
+    // returning atomic sits between a thread's keys.
+    const uint32_t na = (uint32_t)__builtin_popcount(at_t);
+    const uint32_t incl = wave_incl_scan(na);
+    const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    if (wtot) {
+      uint32_t base = 0;
+      if (lane_id() == 0) base = atomicAdd(&s_n, wtot);
+      uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane((int)base) + incl - na;
+#pragma unroll
+      for (int e = 0; e < kFinKeys; ++e) {
+        if (at_t & (1u << e)) {
+          if (pos < (uint32_t)kCandLds) cand[pos] = kk[e];
+          else gkeys[pos] = kk[e];
+          ++pos;
         }
       }
     }
@@ -654,6 +675,11 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     }
   }
   for (int i = (int)ks + tid; i < k; i += kFinThreads) out[i] = -1;
+  // The row histogram is consumed: clear it for the next call (each thread the
+  // bins it read).  Last, so that no store is outstanding while the phases
+  // above wait for their loads (the wait counter covers stores too).
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) ghist[kBins - 1 - (kPer * tid + i)] = 0;
 }
 
 // ---------------------------------------------------------------------------
