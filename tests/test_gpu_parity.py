@@ -160,6 +160,24 @@ def test_edge_lengths_and_dense_equivalence(P):
         check_lse(layer.lse[r].cpu().numpy(), l, f"dense L={L}")
 
 
+@pytest.mark.parametrize("hq,hkv,d,kv,qps,P", [
+    (8, 2, 64, "fp8", 1, 3),      # d = 64 fp8: 4-byte V slices per lane
+    (16, 1, 64, "bf16", 1, 2),    # 16 heads per KV head: 8 waves, d = 64
+    (16, 2, 128, "fp8", 4, 3),    # 32 head rows (4 rows x 8 heads): 4 waves
+    (32, 2, 64, "bf16", 4, 5),    # 64 head rows: 4 waves, d = 64
+    (8, 8, 128, "bf16", 1, 1),    # one head per KV head
+])
+def test_head_dims_dtypes_and_group_sizes(hq, hkv, d, kv, qps, P):
+    """The attention kernel's variants: head dim 64/128, bf16/fp8, head rows
+    per workgroup from 1 to 64 (8 or 4 waves), reuse rows, uneven splits; rows
+    shorter than k blocks and rows with the full k."""
+    shape = QSAShape(hq, hkv, d, 64, 128, 64 if d == 128 else 16, kv_dtype=kv)
+    lens = [1, 3, 4, 67, 300, 1031, 5003]
+    wl = make_workload(shape, lens, step_tokens=qps, q_per_sel=qps, seed=90 + hq + d + qps, device=DEV,
+                       name=f"heads-{hq}/{hkv}-d{d}-{kv}-q{qps}")
+    check_layer(wl, run(wl, P))
+
+
 def test_k_larger_than_blocks_and_small_k():
     shape = QSAShape(8, 2, 64, 32, 7, 16)
     wl = make_workload(shape, [3, 17, 27, 28, 29, 100, 1000], seed=5, device=DEV, name="k7")
