@@ -507,12 +507,11 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
 #pragma unroll
   for (int e = 0; e < kFinKeys; ++e) kk[e] = ckeys[(size_t)cc * kScoreChunk + sub * kFinKeys + e];
   const int Lr = sel_seq_len[s];
-  // keep the compiler from sinking those loads past the length test below
-  asm volatile("" ::"v"(ci), "s"(Lr));
+  // the histogram and the length before the length test below (the keys and
+  // cinfo, loaded after the histogram, are waited for only after the threshold)
+  asm volatile("" ::"s"(Lr));
 #pragma unroll
   for (int i = 0; i < kPer; ++i) asm volatile("" ::"v"(hc[i]));
-#pragma unroll
-  for (int e = 0; e < kFinKeys; ++e) asm volatile("" ::"v"(kk[e]));
 
   const int L = min(Lr, max_seq_len);
   const int nb = max(L, 0) >> 2;
@@ -532,6 +531,9 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   }
   if (tid == 0) { s_n = 0; s_T = 0; s_above = 0; }
   threshold_from_counts<kFinThreads>(hc, ks, sh, &s_T, &s_above);
+  asm volatile("" ::"v"(ci));
+#pragma unroll
+  for (int e = 0; e < kFinKeys; ++e) asm volatile("" ::"v"(kk[e]));
   const int T = s_T;
   const uint32_t above = s_above;
 
