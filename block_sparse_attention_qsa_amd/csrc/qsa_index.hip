@@ -76,7 +76,8 @@ __device__ __forceinline__ int32_t key_score(uint64_t key) {
 }
 
 // Block-wide exclusive prefix sum (blockDim.x threads, a multiple of 64).
-template <int NT>
+// kReuse: end with a barrier, so that sh may be written again right away.
+template <int NT, bool kReuse = true>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh /*[NT/64]*/) {
   const int l = lane_id(), w = threadIdx.x / 64;
   const uint32_t inc = wave_incl_scan(v);
@@ -85,7 +86,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh /*[
   uint32_t off = 0;
 #pragma unroll
   for (int i = 0; i < NT / 64; ++i) off += (i < w) ? sh[i] : 0u;
-  __syncthreads();
+  if (kReuse) __syncthreads();
   return off + inc - v;
 }
 
@@ -100,7 +101,8 @@ __device__ __forceinline__ void threshold_from_counts(const uint32_t (&cnt)[kBin
   uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) mine += cnt[i];
-  uint32_t above = block_excl_scan<NT>(mine, sh);
+  // sh is next written after the barrier below
+  uint32_t above = block_excl_scan<NT, false>(mine, sh);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     if (above < ks && above + cnt[i] >= ks) { *s_T = kBins - 1 - (kPer * tid + i); *s_above = above; }
@@ -666,7 +668,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
   uint32_t cntw = 0;
   for (int i = w0; i < w1; ++i) cntw += (uint32_t)__popcll(bm_lds ? bml[i] : bm[i]);
-  uint32_t pos = block_excl_scan<kFinThreads>(cntw, sh);
+  uint32_t pos = block_excl_scan<kFinThreads, false>(cntw, sh);  // sh is not written again
   for (int i = w0; i < w1; ++i) {
     uint64_t m = bm_lds ? bml[i] : bm[i];
     while (m) {
