@@ -609,7 +609,9 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
 
   // MSB-first radix select of the need-th largest threshold candidate, by
   // wave 0 alone (no workgroup barriers inside).  All of them share the
-  // threshold bin, i.e. key bits 46..63, so the digits start at bit 40.
+  // threshold bin, i.e. key bits 32 + kBinShift and up, so the first digit is
+  // the 8 bits right below (with ~300 candidates over 256 digits, one pass
+  // usually settles it), then 8 bits at a time down to bit 0.
   constexpr uint64_t kBinMask = ~((1ull << (32 + kBinShift)) - 1ull);
   if (tid < 64 && need < n) {
     const int l = tid;
@@ -620,7 +622,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     };
     uint64_t mask = kBinMask, prefix = key_at(0) & kBinMask;
     uint32_t rem = need;
-    for (int shift = 40; shift >= 0; shift -= 8) {
+    for (int shift = 32 + kBinShift - 8;; shift = max(shift - 8, 0)) {
       *reinterpret_cast<uint4*>(&rhist[4 * l]) = uint4{0u, 0u, 0u, 0u};
       wave_lds_sync();
       for (uint32_t i = l; i < n; i += 64) {
@@ -648,7 +650,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
       prefix = (prefix & ~(0xffull << shift)) | ((uint64_t)dsel << shift);
       mask |= 0xffull << shift;
       wave_lds_sync();
-      if (cnt == rem) break;  // every remaining candidate with this prefix is kept
+      if (cnt == rem || shift == 0) break;  // every remaining candidate with this prefix is kept
     }
     if (l == 0) { s_sel[0] = prefix; s_sel[1] = mask; }
   } else if (tid == 0) {
