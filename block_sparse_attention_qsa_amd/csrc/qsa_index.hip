@@ -483,8 +483,9 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   __shared__ uint64_t cand[kCandLds];
   __shared__ uint64_t bml[kWordsLds];
   __shared__ int32_t s_T;
-  __shared__ uint32_t s_above, s_n;
+  __shared__ uint32_t s_above, s_n, s_nfb;
   __shared__ uint64_t s_sel[2];
+  __shared__ uint16_t s_fb[kMaxChunksPerRow];  // chunks read again from their scores
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
   const int nchunks_max = ws.nb_stride / kScoreChunk;
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   } else {
     for (int i = tid; i < nwords; i += kFinThreads) bm[i] = 0;
   }
-  if (tid == 0) { s_n = 0; s_T = 0; s_above = 0; }
+  if (tid == 0) { s_n = 0; s_T = 0; s_above = 0; s_nfb = 0; }
   threshold_from_counts<kFinThreads>(hc, ks, sh, &s_T, &s_above);
   asm volatile("" ::"v"(ci));
 #pragma unroll
@@ -575,11 +576,8 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
         }
         for (uint32_t i = (uint32_t)(tpc * kFinKeys + sub); i < cnt; i += tpc)
           classify(ckeys[(size_t)c * kScoreChunk + i]);
-      } else {  // local bin above T: blocks of bins [T, lb) are not listed; read the chunk's scores
-        for (int i = sub; i < kScoreChunk; i += tpc) {
-          const int j = c * kScoreChunk + i;
-          if (j < nb) classify(cand_key(srow[j], (uint32_t)j));
-        }
+      } else if (sub == 0) {  // local bin above T: bins [T, lb) are not listed; read the chunk's scores below
+        s_fb[atomicAdd(&s_nfb, 1u)] = (uint16_t)c;
       }
     }
     // The first-round threshold candidates are appended with one slot
@@ -603,6 +601,21 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     }
   }
   __syncthreads();
+  // Chunks whose list may be short, one at a time by the whole workgroup: all
+  // its scores are loaded in one round and classified.
+  for (uint32_t f = 0; f < s_nfb; ++f) {
+    const int c = s_fb[f];
+    constexpr int kFbIters = kScoreChunk / kFinThreads;
+    int32_t fs[kFbIters];
+#pragma unroll
+    for (int it = 0; it < kFbIters; ++it) fs[it] = srow[c * kScoreChunk + it * kFinThreads + tid];
+#pragma unroll
+    for (int it = 0; it < kFbIters; ++it) {
+      const int j = c * kScoreChunk + it * kFinThreads + tid;
+      if (j < nb) classify(cand_key(fs[it], (uint32_t)j));
+    }
+  }
+  if (s_nfb) __syncthreads();
   const uint32_t n = s_n;
   const uint32_t need = ks - above;  // 1 <= need <= n
   auto key_at = [&](uint32_t i) -> uint64_t { return i < (uint32_t)kCandLds ? cand[i] : gkeys[i]; };

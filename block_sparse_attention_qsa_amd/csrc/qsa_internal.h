@@ -29,6 +29,7 @@ struct TopkWorkspace {
 };
 
 constexpr int kScoreChunk = 1024;  // micro-blocks per scoring workgroup
+constexpr int kMaxChunksPerRow = (QSA_MAX_SEQ_LEN / 4 + kScoreChunk - 1) / kScoreChunk;
 constexpr int kBins = 2048;        // histogram bins of the score's top bits
 constexpr int kBinShift = 14;      // bin = (score + 2^24) >> 14
 
