@@ -601,21 +601,30 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     }
   }
   __syncthreads();
-  // Chunks whose list may be short, one at a time by the whole workgroup: all
-  // its scores are loaded in one round and classified.
-  for (uint32_t f = 0; f < s_nfb; ++f) {
-    const int c = s_fb[f];
-    constexpr int kFbIters = kScoreChunk / kFinThreads;
-    int32_t fs[kFbIters];
+  // Chunks whose list may be short, by the whole workgroup, up to kFbChunks at
+  // a time: their scores are loaded in one round and classified.
+  constexpr int kFbChunks = 4;
+  constexpr int kFbIters = kScoreChunk / kFinThreads;
+  const uint32_t nfb = s_nfb;
+  for (uint32_t f0 = 0; f0 < nfb; f0 += kFbChunks) {
+    int32_t fs[kFbChunks][kFbIters];
+    int fc[kFbChunks];
 #pragma unroll
-    for (int it = 0; it < kFbIters; ++it) fs[it] = srow[c * kScoreChunk + it * kFinThreads + tid];
+    for (int q = 0; q < kFbChunks; ++q) {
+      fc[q] = s_fb[min(f0 + q, nfb - 1)];  // past the list: the last chunk again, not classified
 #pragma unroll
-    for (int it = 0; it < kFbIters; ++it) {
-      const int j = c * kScoreChunk + it * kFinThreads + tid;
-      if (j < nb) classify(cand_key(fs[it], (uint32_t)j));
+      for (int it = 0; it < kFbIters; ++it) fs[q][it] = srow[fc[q] * kScoreChunk + it * kFinThreads + tid];
+    }
+#pragma unroll
+    for (int q = 0; q < kFbChunks; ++q) {
+#pragma unroll
+      for (int it = 0; it < kFbIters; ++it) {
+        const int j = fc[q] * kScoreChunk + it * kFinThreads + tid;
+        if (f0 + q < nfb && j < nb) classify(cand_key(fs[q][it], (uint32_t)j));
+      }
     }
   }
-  if (s_nfb) __syncthreads();
+  if (nfb) __syncthreads();
   const uint32_t n = s_n;
   const uint32_t need = ks - above;  // 1 <= need <= n
   auto key_at = [&](uint32_t i) -> uint64_t { return i < (uint32_t)kCandLds ? cand[i] : gkeys[i]; };
