@@ -38,8 +38,6 @@ namespace {
 
 constexpr int kScoreThreads = 512;                     // score kernel
 constexpr int kScoreIters = kScoreChunk / kScoreThreads;
-constexpr int kCandThreads = 256;                      // chunk-candidate kernel (prefill)
-constexpr int kCandIters = kScoreChunk / kCandThreads;
 
 struct WsPtrs {
   int32_t* scores;
@@ -431,40 +429,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
                                                &s_lb, &s_cnt);
 }
 
-// Chunk candidates from stored scores (grid: chunk x row; prefill, whose
-// scoring kernel covers 16 rows at a time): the chunk's histogram in LDS, then
-// the same candidate list as the decode scan writes.
-__global__ __launch_bounds__(kCandThreads) void chunk_cand_kernel(
-    const int32_t* __restrict__ sel_seq_len, int32_t max_seq_len, WsPtrs ws) {
-  __shared__ uint32_t hist[kBins];
-  __shared__ int32_t s_lb;
-  __shared__ uint32_t s_cnt;
-  __shared__ int s_maxbin;
-  const int s = blockIdx.y;
-  const int c = blockIdx.x;
-  const int L = min(sel_seq_len[s], max_seq_len);
-  const int nb = max(L, 0) >> 2;
-  if (c * kScoreChunk >= nb) return;
-  const int32_t* srow = ws.scores + (size_t)s * ws.nb_stride;
-  int32_t sc[kCandIters];  // unconditional loads: slots past the row's end exist and are masked
-#pragma unroll
-  for (int it = 0; it < kCandIters; ++it) sc[it] = srow[c * kScoreChunk + it * kCandThreads + threadIdx.x];
-  for (int i = threadIdx.x; i < kBins; i += kCandThreads) hist[i] = 0;
-  if (threadIdx.x == 0) s_maxbin = -1;
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < kCandIters; ++it) {
-    const int j = c * kScoreChunk + it * kCandThreads + threadIdx.x;
-    atomicAdd(&hist[score_bin(sc[it])], j < nb ? 1u : 0u);
-  }
-  note_max_bin<kCandIters>(sc, c, kCandThreads, nb, &s_maxbin);
-  __syncthreads();
-  chunk_candidates<kCandThreads, kCandIters>(hist, s_maxbin, sc, c, nb, ws.nb_stride,
-                                             ws.keys + (size_t)s * ws.nb_stride + (size_t)c * kScoreChunk,
-                                             ws.cinfo + (size_t)s * (ws.nb_stride / kScoreChunk) + c,
-                                             &s_lb, &s_cnt);
-}
-
 // Finalize (one workgroup per selecting row): the row's threshold bin T from
 // its histogram; the chunks' candidate lists (one round of loads, issued before
 // the row length is known) are classified: bin > T -> selected (LDS bitmap),
@@ -720,9 +684,10 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
 // score = q.s + 256 q.h - 384 sum(q) exactly in int32.  The B operand of lane l
 // is the 16-byte s-plane chunk l/16 of block l%16: a plain 16-byte load from
 // the page, no LDS.  Per-row histograms (16-bit counts, two per LDS word) are
-// merged into the rows' histograms as in the decode scan; a chunk-candidate
-// kernel then writes the chunks' candidate lists from the stored scores, and
-// the finalize selects exactly as for qsa_index_topk.
+// merged into the rows' histograms as in the decode scan, and from them each
+// row's candidate list for the chunk is written from the scores still in
+// registers (the scores are stored too, for rows whose list may be short);
+// the finalize then selects exactly as for qsa_index_topk.
 constexpr int kPfThreads = 256;
 constexpr int kPfRows = 16;
 constexpr int kPfTiles = kScoreChunk / (kPfThreads / 64) / 16;  // block tiles per wave
@@ -810,9 +775,15 @@ __global__ __launch_bounds__(kPfThreads) void prefill_score_kernel(
       m1[t][ks] = *reinterpret_cast<const uint16_t*>(mp + D / 8 + 2 * ch);
     }
   }
+  __shared__ int s_pmax[kPfRows];       // per row: highest bin of its valid scores in this chunk
+  __shared__ int s_plb[kPfRows];        // per row: local bin of its candidate list
+  __shared__ uint32_t s_pcnt[kPfRows];  // per row: list length
   for (int i = threadIdx.x; i < kPfRows * kBins / 2; i += kPfThreads) hist[i] = 0;
+  if (threadIdx.x < kPfRows) { s_pmax[threadIdx.x] = -1; s_pcnt[threadIdx.x] = 0; }
   __syncthreads();
 
+  int32_t scv[kPfTiles][4];  // the scores stay here for the candidate lists
+  int mb[4] = {-1, -1, -1, -1};
 #pragma unroll
   for (int t = 0; t < kPfTiles; ++t) {
     i32x4 cs = {0, 0, 0, 0}, chh = {0, 0, 0, 0};
@@ -837,8 +808,20 @@ __global__ __launch_bounds__(kPfThreads) void prefill_score_kernel(
       const bool valid = j < nb_m[i];  // rows past the request's end have nb 0
       const int bin = score_bin(sc);
       atomicAdd(&hist[(m * kBins + bin) >> 1], valid ? ((bin & 1) ? 0x10000u : 1u) : 0u);
+      mb[i] = max(mb[i], valid ? bin : -1);
+      scv[t][i] = sc;
       if (r < r_end) ws.scores[(size_t)r * ws.nb_stride + j] = sc;
     }
+  }
+  // highest bin per row: the 16 lanes of a lane group (one DPP row) share its rows
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int v = mb[i];
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x111, 0xf, 0xf, false));  // row_shr:1
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x112, 0xf, 0xf, false));  // row_shr:2
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x114, 0xf, 0xf, false));  // row_shr:4
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x118, 0xf, 0xf, false));  // row_shr:8
+    if (col == 15) atomicMax(&s_pmax[4 * g + i], v);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < kPfRows * kBins / 2; i += kPfThreads) {
@@ -848,6 +831,57 @@ __global__ __launch_bounds__(kPfThreads) void prefill_score_kernel(
       uint32_t* gh = ws.hist + (size_t)(r0 + m) * kBins + bin;
       if (h & 0xffffu) atomicAdd(gh, h & 0xffffu);
       if (h >> 16) atomicAdd(gh + 1, h >> 16);
+    }
+  }
+  // Each row's candidate list for this chunk, as the decode scan writes it
+  // (chunk_candidates): the local bin of its m-th best valid block, found by
+  // wave w for rows w, w + 4, w + 8, w + 12 walking down from the row's
+  // highest bin; then every valid block at or above it.
+  const int lm = local_m(ws.nb_stride);
+  for (int m = w; m < kPfRows; m += kPfThreads / 64) {
+    const int nbr = __shfl(nbc, m, 64);  // lane m holds row r0 + m's length
+    const int valid_total = min(kScoreChunk, nbr - c * kScoreChunk);
+    if (valid_total <= 0) continue;       // uniform: the row ends before this chunk
+    const uint32_t mm = (uint32_t)min(lm, valid_total);
+    int top = s_pmax[m], lb = 0;
+    uint32_t acc = 0;
+    bool found = false;
+    while (!found && top >= 0) {
+      const int bin = top - lane;
+      const uint32_t cnt = bin >= 0 ? (hist[(m * kBins + bin) >> 1] >> (16 * (bin & 1))) & 0xffffu : 0u;
+      const uint32_t inc = wave_incl_scan(cnt) + acc;
+      const uint64_t hit = __ballot(inc >= mm);
+      if (hit) {
+        found = true;
+        lb = top - (__ffsll((long long)hit) - 1);
+      } else {
+        acc = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+        top -= 64;
+      }
+    }
+    if (lane == 0) s_plb[m] = lb;
+  }
+  __syncthreads();
+  {
+    const int nch = ws.nb_stride / kScoreChunk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * g + i;
+      if (r0 + m >= r_end) continue;
+      const int lb = s_plb[m];  // set for every row that reaches this chunk
+      uint64_t* keys = ws.keys + (size_t)(r0 + m) * ws.nb_stride + (size_t)c * kScoreChunk;
+#pragma unroll
+      for (int t = 0; t < kPfTiles; ++t) {
+        const int j = jw + 16 * t + col;
+        if (j < nb_m[i] && score_bin(scv[t][i]) >= lb) keys[atomicAdd(&s_pcnt[m], 1u)] = cand_key(scv[t][i], (uint32_t)j);
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < kPfRows) {
+      const int m = threadIdx.x;
+      const int nbr = nbc;  // lane m of wave 0 holds row r0 + m's length
+      if (r0 + m < r_end && nbr > c * kScoreChunk)
+        ws.cinfo[(size_t)(r0 + m) * nch + c] = (s_pcnt[m] << 16) | (uint32_t)s_plb[m];
     }
   }
 }
@@ -1009,10 +1043,6 @@ qsa_status launch_prefill_index_topk(const qsa_config& c, int32_t B, int32_t R, 
   }
   qsa_status st = check_launch("qsa_prefill_index_topk(score)");
   if (st != QSA_OK || topk == nullptr) return st;
-  hipLaunchKernelGGL(chunk_cand_kernel, dim3(chunks, R), dim3(kCandThreads), 0, stream, row_seq_len,
-                     max_seq_len, ws);
-  st = check_launch("qsa_prefill_index_topk(candidates)");
-  if (st != QSA_OK) return st;
   hipLaunchKernelGGL(finalize_kernel, dim3(R), dim3(kFinThreads), 0, stream, row_seq_len, c.topk_blocks,
                      max_seq_len, topk, ws);
   return check_launch("qsa_prefill_index_topk(finalize)");
