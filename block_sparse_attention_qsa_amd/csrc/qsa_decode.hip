@@ -36,10 +36,13 @@ namespace qsa {
 
 namespace {
 
-// Waves per workgroup: 8 (one 16-slot tile each for a split of 32 blocks)
-// while the per-wave output staging fits the LDS, else 4.
-template <int D, int NH>
-constexpr int decode_waves() { return NH <= 16 ? 8 : 4; }
+// Waves per workgroup: 8 (one 16-slot tile each for a split of 32 blocks) when
+// the grid has fewer workgroups than two per CU and the per-wave output
+// staging fits the LDS; else 4, so that two workgroups share a CU and one's
+// tail overlaps the other's loads.
+constexpr int kDecodeWideMaxGroups = 512;
+template <int NH>
+constexpr bool decode_wide_ok() { return NH <= 16; }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -110,9 +113,9 @@ __device__ __forceinline__ float sum_lg(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, int NH, bool FP8>
-__global__ __launch_bounds__((decode_waves<D, NH>() * 64)) void decode_kernel(DecodeArgs a) {
-  constexpr int kWaves = decode_waves<D, NH>();
+template <int D, int NH, bool FP8, int W>
+__global__ __launch_bounds__(W * 64) void decode_kernel(DecodeArgs a) {
+  constexpr int kWaves = W;
   constexpr int kThreads = kWaves * 64;
   constexpr int NT = (NH + 15) / 16;  // MFMA tiles of 16 heads
   constexpr int NHP = NT * 16;        // heads padded to whole tiles
@@ -480,7 +483,14 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ o_p
 
 template <int D, int NH, bool FP8>
 qsa_status launch_decode_t(dim3 grid, const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, NH, FP8>), grid, dim3(decode_waves<D, NH>() * 64), 0, stream, a);
+  const int64_t groups = (int64_t)grid.x * grid.y * grid.z;
+  if constexpr (decode_wide_ok<NH>()) {
+    if (groups < kDecodeWideMaxGroups) {
+      hipLaunchKernelGGL((decode_kernel<D, NH, FP8, 8>), grid, dim3(8 * 64), 0, stream, a);
+      return check_launch("qsa_sparse_decode");
+    }
+  }
+  hipLaunchKernelGGL((decode_kernel<D, NH, FP8, 4>), grid, dim3(4 * 64), 0, stream, a);
   return check_launch("qsa_sparse_decode");
 }
 
