@@ -443,12 +443,12 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     int32_t* __restrict__ topk, WsPtrs ws) {
   constexpr int kPer = kBins / kFinThreads;
   __shared__ uint32_t sh[kFinThreads / 64];
-  __shared__ __align__(16) uint32_t rhist[256];
+  constexpr int kRadixPasses = (32 + kBinShift + 7) / 8;  // 8-bit digits below the threshold bin
+  __shared__ __align__(16) uint32_t rhist[kRadixPasses][256];
   __shared__ uint64_t cand[kCandLds];
   __shared__ uint64_t bml[kWordsLds];
   __shared__ int32_t s_T;
   __shared__ uint32_t s_above, s_n, s_nfb;
-  __shared__ uint64_t s_sel[2];
   __shared__ uint16_t s_fb[kMaxChunksPerRow];  // chunks read again from their scores
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
@@ -496,6 +496,8 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   } else {
     for (int i = tid; i < nwords; i += kFinThreads) bm[i] = 0;
   }
+  for (int i = tid; i < kRadixPasses * 64; i += kFinThreads)
+    reinterpret_cast<uint4*>(&rhist[0][0])[i] = uint4{0u, 0u, 0u, 0u};
   if (tid == 0) { s_n = 0; s_T = 0; s_above = 0; s_nfb = 0; }
   threshold_from_counts<kFinThreads>(hc, ks, sh, &s_T, &s_above);
   asm volatile("" ::"v"(ci));
@@ -593,59 +595,55 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   const uint32_t need = ks - above;  // 1 <= need <= n
   auto key_at = [&](uint32_t i) -> uint64_t { return i < (uint32_t)kCandLds ? cand[i] : gkeys[i]; };
 
-  // MSB-first radix select of the need-th largest threshold candidate, by
-  // wave 0 alone (no workgroup barriers inside).  All of them share the
-  // threshold bin, i.e. key bits 32 + kBinShift and up, so the first digit is
-  // the 8 bits right below (with ~300 candidates over 256 digits, one pass
-  // usually settles it), then 8 bits at a time down to bit 0.
+  // MSB-first radix select of the need-th largest threshold candidate by the
+  // whole workgroup.  All candidates share the threshold bin, i.e. key bits
+  // 32 + kBinShift and up, so the first digit is the 8 bits right below (with
+  // ~300 candidates over 256 digits, one pass usually settles it), then 8 bits
+  // at a time down to bit 0.  Each thread holds one candidate in a register
+  // (any beyond the workgroup's size are read again per pass).  Every pass
+  // counts into a histogram of its own, cleared with the bitmap above, so one
+  // barrier per pass suffices: after it every wave reads the same counts and
+  // finds the digit by itself.
   constexpr uint64_t kBinMask = ~((1ull << (32 + kBinShift)) - 1ull);
-  if (tid < 64 && need < n) {
-    const int l = tid;
-    auto wave_lds_sync = []() {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-    uint64_t mask = kBinMask, prefix = key_at(0) & kBinMask;
+  const uint64_t mine = key_at(min((uint32_t)tid, n - 1));
+  uint64_t prefix = 0, mask = 0;  // (mask 0 keeps every candidate)
+  if (need < n) {
+    const int l = lane_id();
+    mask = kBinMask;
+    prefix = cand[0] & kBinMask;
     uint32_t rem = need;
-    for (int shift = 32 + kBinShift - 8;; shift = max(shift - 8, 0)) {
-      *reinterpret_cast<uint4*>(&rhist[4 * l]) = uint4{0u, 0u, 0u, 0u};
-      wave_lds_sync();
-      for (uint32_t i = l; i < n; i += 64) {
+    for (int p = 0, shift = 32 + kBinShift - 8;; ++p, shift = max(shift - 8, 0)) {
+      uint32_t* h = rhist[p];
+      if ((uint32_t)tid < n && (mine & mask) == prefix) atomicAdd(&h[(mine >> shift) & 0xff], 1u);
+      for (uint32_t i = tid + kFinThreads; i < n; i += kFinThreads) {
         const uint64_t key = key_at(i);
-        if ((key & mask) == prefix) atomicAdd(&rhist[(key >> shift) & 0xff], 1u);
+        if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 0xff], 1u);
       }
-      wave_lds_sync();
+      __syncthreads();
       // lane l owns digits 255-4l .. 252-4l (descending)
-      const uint4 hv = *reinterpret_cast<const uint4*>(&rhist[252 - 4 * l]);
+      const uint4 hv = *reinterpret_cast<const uint4*>(&h[252 - 4 * l]);
       const uint32_t cs[4] = {hv.w, hv.z, hv.y, hv.x};
       const uint32_t tot = cs[0] + cs[1] + cs[2] + cs[3];
       uint32_t acc = wave_incl_scan(tot) - tot;  // count in larger digits
       uint32_t dsel = 0, larger = 0, cnt = 0;
-      bool mine = false;
+      bool found = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (!mine && acc < rem && acc + cs[i] >= rem) { mine = true; dsel = 255 - 4 * l - i; larger = acc; cnt = cs[i]; }
+        if (!found && acc < rem && acc + cs[i] >= rem) { found = true; dsel = 255 - 4 * l - i; larger = acc; cnt = cs[i]; }
         acc += cs[i];
       }
-      const int src = __ffsll((long long)__ballot(mine)) - 1;
+      const int src = __ffsll((long long)__ballot(found)) - 1;
       dsel = (uint32_t)__builtin_amdgcn_readlane((int)dsel, src);
       larger = (uint32_t)__builtin_amdgcn_readlane((int)larger, src);
       cnt = (uint32_t)__builtin_amdgcn_readlane((int)cnt, src);
       rem -= larger;
       prefix = (prefix & ~(0xffull << shift)) | ((uint64_t)dsel << shift);
       mask |= 0xffull << shift;
-      wave_lds_sync();
       if (cnt == rem || shift == 0) break;  // every remaining candidate with this prefix is kept
     }
-    if (l == 0) { s_sel[0] = prefix; s_sel[1] = mask; }
-  } else if (tid == 0) {
-    s_sel[0] = 0;  // keep every candidate
-    s_sel[1] = 0;
   }
-  __syncthreads();
-  const uint64_t prefix = s_sel[0], mask = s_sel[1];
-  for (uint32_t i = tid; i < n; i += kFinThreads) {
+  if ((uint32_t)tid < n && (mine & mask) >= prefix) mark(0xffffffffu - (uint32_t)(mine & 0xffffffffull));
+  for (uint32_t i = tid + kFinThreads; i < n; i += kFinThreads) {
     const uint64_t key = key_at(i);
     if ((key & mask) >= prefix) mark(0xffffffffu - (uint32_t)(key & 0xffffffffull));
   }
