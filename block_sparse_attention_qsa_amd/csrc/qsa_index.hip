@@ -438,6 +438,10 @@ constexpr int kFinThreads = 512;
 constexpr int kCandLds = 4096;   // threshold candidates held in LDS (more: workspace)
 constexpr int kWordsLds = 4096;  // bitmap words held in LDS (rows up to 262,144 blocks)
 
+// kBmLds: the selection bitmap of every row fits the LDS (the host picks it
+// from the workspace's row stride), so no mark or read of it branches on where
+// it lives.
+template <bool kBmLds>
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     const int32_t* __restrict__ sel_seq_len, int32_t k, int32_t max_seq_len,
     int32_t* __restrict__ topk, WsPtrs ws) {
@@ -446,7 +450,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   constexpr int kRadixPasses = (32 + kBinShift + 7) / 8;  // 8-bit digits below the threshold bin
   __shared__ __align__(16) uint32_t rhist[kRadixPasses][256];
   __shared__ uint64_t cand[kCandLds];
-  __shared__ uint64_t bml[kWordsLds];
+  __shared__ uint64_t bml[kBmLds ? kWordsLds : 1];
   __shared__ int32_t s_T;
   __shared__ uint32_t s_above, s_n, s_nfb;
   __shared__ uint16_t s_fb[kMaxChunksPerRow];  // chunks read again from their scores
@@ -490,7 +494,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   const uint32_t ks = (uint32_t)min(k, nb);
   const int nchunks = (nb + kScoreChunk - 1) / kScoreChunk;
   const int nwords = (nb + 63) >> 6;
-  const bool bm_lds = nwords <= kWordsLds;
+  constexpr bool bm_lds = kBmLds;  // then nwords <= nb_stride / 64 <= kWordsLds
   if (bm_lds) {
     for (int i = tid; i < nwords; i += kFinThreads) bml[i] = 0;
   } else {
@@ -555,13 +559,22 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     if (wtot) {
       uint32_t base = 0;
       if (lane_id() == 0) base = atomicAdd(&s_n, wtot);
-      uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane((int)base) + incl - na;
+      base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+      uint32_t pos = base + incl - na;
+      if (base + wtot <= (uint32_t)kCandLds) {  // the usual case: all in LDS, no branch per key
 #pragma unroll
-      for (int e = 0; e < kFinKeys; ++e) {
-        if (at_t & (1u << e)) {
-          if (pos < (uint32_t)kCandLds) cand[pos] = kk[e];
-          else gkeys[pos] = kk[e];
-          ++pos;
+        for (int e = 0; e < kFinKeys; ++e) {
+          if (at_t & (1u << e)) cand[pos] = kk[e];
+          pos += (at_t >> e) & 1u;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < kFinKeys; ++e) {
+          if (at_t & (1u << e)) {
+            if (pos < (uint32_t)kCandLds) cand[pos] = kk[e];
+            else gkeys[pos] = kk[e];
+            ++pos;
+          }
         }
       }
     }
@@ -958,6 +971,17 @@ qsa_status launch_scan(const qsa_config& c, dim3 grid, const int8_t* q_index, co
   return QSA_OK;
 }
 
+qsa_status launch_finalize(int32_t rows, const int32_t* seq_len, int32_t k, int32_t max_seq_len, int32_t* topk,
+                           const WsPtrs& ws, hipStream_t stream, const char* what) {
+  if (ws.nb_stride / 64 <= kWordsLds)
+    hipLaunchKernelGGL(finalize_kernel<true>, dim3(rows), dim3(kFinThreads), 0, stream, seq_len, k, max_seq_len,
+                       topk, ws);
+  else
+    hipLaunchKernelGGL(finalize_kernel<false>, dim3(rows), dim3(kFinThreads), 0, stream, seq_len, k, max_seq_len,
+                       topk, ws);
+  return check_launch(what);
+}
+
 }  // namespace
 
 qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len,
@@ -973,9 +997,7 @@ qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len
   if (st != QSA_OK) return st;
   st = check_launch("qsa_index_topk(score)");
   if (st != QSA_OK || topk == nullptr) return st;
-  hipLaunchKernelGGL(finalize_kernel, dim3(S), dim3(kFinThreads), 0, stream, sel_seq_len, c.topk_blocks,
-                     max_seq_len, topk, ws);
-  return check_launch("qsa_index_topk(finalize)");
+  return launch_finalize(S, sel_seq_len, c.topk_blocks, max_seq_len, topk, ws, stream, "qsa_index_topk(finalize)");
 }
 
 qsa_status launch_compress_index_topk(const qsa_config& c, int32_t num_reqs, const int8_t* new_keys,
@@ -1008,9 +1030,8 @@ qsa_status launch_compress_index_topk(const qsa_config& c, int32_t num_reqs, con
   if (st != QSA_OK) return st;
   st = check_launch("qsa_compress_index_topk(append+score)");
   if (st != QSA_OK || topk == nullptr) return st;
-  hipLaunchKernelGGL(finalize_kernel, dim3(S), dim3(kFinThreads), 0, stream, sel_seq_len, c.topk_blocks,
-                     max_seq_len, topk, ws);
-  return check_launch("qsa_compress_index_topk(finalize)");
+  return launch_finalize(S, sel_seq_len, c.topk_blocks, max_seq_len, topk, ws, stream,
+                         "qsa_compress_index_topk(finalize)");
 }
 
 qsa_status launch_prefill_index_topk(const qsa_config& c, int32_t B, int32_t R, int32_t max_rows,
@@ -1041,9 +1062,8 @@ qsa_status launch_prefill_index_topk(const qsa_config& c, int32_t B, int32_t R, 
   }
   qsa_status st = check_launch("qsa_prefill_index_topk(score)");
   if (st != QSA_OK || topk == nullptr) return st;
-  hipLaunchKernelGGL(finalize_kernel, dim3(R), dim3(kFinThreads), 0, stream, row_seq_len, c.topk_blocks,
-                     max_seq_len, topk, ws);
-  return check_launch("qsa_prefill_index_topk(finalize)");
+  return launch_finalize(R, row_seq_len, c.topk_blocks, max_seq_len, topk, ws, stream,
+                         "qsa_prefill_index_topk(finalize)");
 }
 
 }  // namespace qsa
