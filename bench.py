@@ -6,9 +6,11 @@ A step is one decode step of every layer in a stack of `--layers` independent
 QSA layers (default 12, the number of QSA layers in the 48-layer model the
 pages describe), each layer running the whole hot path on its own caches:
 
-    qsa_compress_index_topk -> qsa_sparse_decode -> qsa_merge_partials
+    qsa_compress_index_topk (scan only) -> qsa_select_sparse_decode -> qsa_merge_partials
 
-(--no-fuse: qsa_compress, then qsa_index_topk, for the separate calls)
+(--no-fuse: qsa_compress, then the scan of qsa_index_topk; --no-select-fuse:
+the selection in qsa_compress_index_topk / qsa_index_topk, then
+qsa_sparse_decode)
 
 The per-layer caches (about 84 MB touched per layer at 256k context) rotate so
 that one step touches about 1 GB, far beyond the 256 MB Infinity Cache.  The
@@ -277,7 +279,7 @@ def prefill_bench(args):
     for li in range(nl):
         wl = make_prefill_workload(SHAPE_MAIN, [65536] * 4, 512, seed=7000 + li, device="cuda",
                                    name="prefill-64k-chunk512")
-        layer = QSAPrefill(wl, num_splits=P)
+        layer = QSAPrefill(wl, num_splits=P, select_decode=not args.no_select_fuse)
         layer.prefill()
         layers.append(layer)
         print(f"[bench] prefill layer {li} ready (rows={wl.num_rows})", file=sys.stderr, flush=True)
@@ -407,6 +409,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-fuse", action="store_true",
                     help="append with qsa_compress, then qsa_index_topk (two scans' worth of launches)")
+    ap.add_argument("--no-select-fuse", action="store_true",
+                    help="select in the index call, then qsa_sparse_decode (instead of qsa_select_sparse_decode)")
     ap.add_argument("--kernel-iters", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -448,7 +452,7 @@ def main():
     layers = []
     for li in range(args.layers):
         wl = named_workload(cfg, device=dev, seed=None if li == 0 else 1000 * cfg + li)
-        layer = QSALayer(wl, num_splits=P, fuse_append=not args.no_fuse)
+        layer = QSALayer(wl, num_splits=P, fuse_append=not args.no_fuse, select_decode=not args.no_select_fuse)
         layer.prefill()
         layers.append(layer)
         print(f"[bench] layer {li} ready ({wl.name}, rows={wl.num_rows})", file=sys.stderr, flush=True)
@@ -560,6 +564,8 @@ def main():
         "config": {"workload": f"cfg{cfg} {DESCR[cfg]}", "layers_per_step": args.layers,
                    "query_rows_per_layer": wl0.num_rows, "splits": P, "hip_graph": graph is not None,
                    "append": "fused into the scan" if fused else "separate qsa_compress launch",
+                   "selection": ("with the attention (qsa_select_sparse_decode)" if layers[0].select_decode
+                                 else "separate finalize launch"),
                    "index_arith": "int8 dot4 -> int32 (exact)", "attention_arith": "bf16 MFMA / fp32 softmax"},
         "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
                      "frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,

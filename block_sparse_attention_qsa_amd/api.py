@@ -178,6 +178,27 @@ def qsa_sparse_decode(cfg: QSAConfig, q: torch.Tensor, row_seq_len: torch.Tensor
                                          _ptr(o_part), _ptr(lse_part), _stream(stream)))
 
 
+def qsa_select_sparse_decode(cfg: QSAConfig, q: torch.Tensor, row_seq_len: torch.Tensor,
+                             sel_req: torch.Tensor, sel_seq_len: torch.Tensor, block_table: torch.Tensor,
+                             k_cache: torch.Tensor, v_cache: torch.Tensor, topk: torch.Tensor,
+                             o_part: torch.Tensor, lse_part: torch.Tensor, workspace: torch.Tensor,
+                             max_seq_len: int, q_per_sel: int = 1, k_scale: Optional[torch.Tensor] = None,
+                             v_scale: Optional[torch.Tensor] = None, stream=None) -> None:
+    """The selection of a scored workspace (left by an index call with topk=None) into topk, then
+    qsa_sparse_decode on it: o_part fp32 [P, R, H_q, d], lse_part fp32 [P, R, H_q]."""
+    _dt(q, torch.bfloat16); _dt(o_part, torch.float32); _dt(lse_part, torch.float32)
+    _dt(row_seq_len, torch.int32); _dt(sel_req, torch.int32); _dt(sel_seq_len, torch.int32)
+    _dt(topk, torch.int32); _dt(block_table, torch.int32)
+    c = cfg.to_c()
+    S = sel_req.shape[0]
+    P = o_part.shape[0]
+    _check(_lib.load().qsa_select_sparse_decode(
+        ctypes.byref(c), S, int(q_per_sel), P, int(max_seq_len), _ptr(q), _ptr(row_seq_len), _ptr(sel_req),
+        _ptr(sel_seq_len), _ptr(block_table), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(topk), _ptr(o_part), _ptr(lse_part), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
 def qsa_merge_partials(o_part: torch.Tensor, lse_part: torch.Tensor, out: torch.Tensor,
                        lse: torch.Tensor, stream=None) -> None:
     """LSE merge: out fp32 or bf16 [R, H, d] (by out's dtype), lse fp32 [R, H]."""

@@ -218,15 +218,16 @@ qsa_status qsa_prefill_index_topk(const qsa_config* cfg, int32_t num_reqs, int32
                                    row_seq_len, block_table, ckey_cache, topk, lay, workspace, stream);
 }
 
-qsa_status qsa_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_t q_per_sel,
-                             int32_t num_splits, const void* q, const int32_t* row_seq_len,
-                             const int32_t* sel_req, const int32_t* sel_seq_len,
-                             const int32_t* topk, const int32_t* block_table,
-                             const void* k_cache, const void* v_cache,
-                             const float* k_scale, const float* v_scale,
-                             float* o_part, float* lse_part, hipStream_t stream) {
-  qsa_status st = check_config(cfg, false, true);
-  if (st != QSA_OK) return st;
+}  // extern "C"
+
+// Argument checks of the attention half (qsa_sparse_decode and the fused call);
+// `what` names the call in the messages.
+static qsa_status check_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_t q_per_sel, int32_t num_splits,
+                               const void* q, const int32_t* row_seq_len, const int32_t* sel_req,
+                               const int32_t* sel_seq_len, const int32_t* topk, const int32_t* block_table,
+                               const void* k_cache, const void* v_cache, const float* k_scale,
+                               const float* v_scale, const float* o_part, const float* lse_part,
+                               const char* what) {
   if (num_sel_rows < 0 || num_sel_rows > 65535)
     return fail(QSA_ERR_INVALID_ARGUMENT, "num_sel_rows must be in [0, 65535] (got %d)", num_sel_rows);
   if (num_splits < 1 || num_splits > 64)
@@ -241,16 +242,59 @@ qsa_status qsa_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_
   if (num_sel_rows == 0) return QSA_OK;
   if (!q || !row_seq_len || !sel_req || !sel_seq_len || !topk || !block_table || !k_cache || !v_cache ||
       !o_part || !lse_part)
-    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_sparse_decode: NULL array argument");
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL array argument", what);
   if (cfg->kv_dtype == QSA_KV_FP8_E4M3 && (!k_scale || !v_scale))
-    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_sparse_decode: fp8 K/V need k_scale and v_scale");
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: fp8 K/V need k_scale and v_scale", what);
   if (cfg->kv_dtype == QSA_KV_FP8_E4M3 && (!aligned(k_scale, 16) || !aligned(v_scale, 16)))
-    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_sparse_decode: k_scale and v_scale need 16-byte alignment");
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: k_scale and v_scale need 16-byte alignment", what);
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
-    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_sparse_decode: q, k_cache, v_cache need 16-byte alignment");
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: q, k_cache, v_cache need 16-byte alignment", what);
+  return QSA_OK;
+}
+
+extern "C" {
+
+qsa_status qsa_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_t q_per_sel,
+                             int32_t num_splits, const void* q, const int32_t* row_seq_len,
+                             const int32_t* sel_req, const int32_t* sel_seq_len,
+                             const int32_t* topk, const int32_t* block_table,
+                             const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale,
+                             float* o_part, float* lse_part, hipStream_t stream) {
+  qsa_status st = check_config(cfg, false, true);
+  if (st != QSA_OK) return st;
+  st = check_decode(cfg, num_sel_rows, q_per_sel, num_splits, q, row_seq_len, sel_req, sel_seq_len, topk,
+                    block_table, k_cache, v_cache, k_scale, v_scale, o_part, lse_part, "qsa_sparse_decode");
+  if (st != QSA_OK || num_sel_rows == 0) return st;
   return launch_sparse_decode(*cfg, num_sel_rows, q_per_sel, num_splits, q, row_seq_len, sel_req,
                               sel_seq_len, topk, block_table, k_cache, v_cache, k_scale, v_scale,
                               o_part, lse_part, stream);
+}
+
+qsa_status qsa_select_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_t q_per_sel,
+                                    int32_t num_splits, int32_t max_seq_len, const void* q,
+                                    const int32_t* row_seq_len, const int32_t* sel_req,
+                                    const int32_t* sel_seq_len, const int32_t* block_table,
+                                    const void* k_cache, const void* v_cache,
+                                    const float* k_scale, const float* v_scale, int32_t* topk,
+                                    float* o_part, float* lse_part,
+                                    void* workspace, size_t ws_bytes, hipStream_t stream) {
+  qsa_status st = check_config(cfg, true, true);
+  if (st != QSA_OK) return st;
+  if (max_seq_len < 0 || max_seq_len > QSA_MAX_SEQ_LEN)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "max_seq_len must be in [0, %d] (got %d)", QSA_MAX_SEQ_LEN, max_seq_len);
+  st = check_decode(cfg, num_sel_rows, q_per_sel, num_splits, q, row_seq_len, sel_req, sel_seq_len, topk,
+                    block_table, k_cache, v_cache, k_scale, v_scale, o_part, lse_part, "qsa_select_sparse_decode");
+  if (st != QSA_OK || num_sel_rows == 0) return st;
+  TopkWorkspace lay = topk_workspace_layout(num_sel_rows, max_seq_len);
+  if (!workspace) return fail(QSA_ERR_WORKSPACE, "qsa_select_sparse_decode: workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(QSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < lay.total)
+    return fail(QSA_ERR_WORKSPACE, "qsa_select_sparse_decode: workspace has %zu bytes, needs %zu", ws_bytes,
+                lay.total);
+  return launch_select_decode(*cfg, num_sel_rows, q_per_sel, num_splits, max_seq_len, q, row_seq_len, sel_req,
+                              sel_seq_len, block_table, k_cache, v_cache, k_scale, v_scale, topk, o_part,
+                              lse_part, lay, workspace, stream);
 }
 
 qsa_status qsa_merge_partials(int32_t num_splits, int32_t num_rows, int32_t num_heads,

@@ -31,6 +31,7 @@
 // multiplies the logit and the V scale multiplies the probability.
 #include "qsa_device.h"
 #include "qsa_internal.h"
+#include "qsa_select.h"
 
 namespace qsa {
 
@@ -113,8 +114,18 @@ __device__ __forceinline__ float sum_lg(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, int NH, bool FP8, int W>
-__global__ __launch_bounds__(W * 64) void decode_kernel(DecodeArgs a) {
+// Where the fused kernel's selection lives (LDS), for decode_body.
+struct SelView {
+  const int32_t* sel;  // the row's k selected block ids (ascending, -1 padded)
+  const int32_t* bt;   // the request's first nbt page-table entries
+  int nbt;
+};
+
+// The attention of one workgroup (split p, KV head kvh, selecting row s).
+// kFusedSel: the selection is not read from a.topk; select_fn(b) computes it
+// once the workgroup's own loads are in flight and returns where it is.
+template <int D, int NH, bool FP8, int W, bool kFusedSel, class SelectFn>
+__device__ __forceinline__ void decode_body(const DecodeArgs& a, SelectFn&& select_fn) {
   constexpr int kWaves = W;
   constexpr int kThreads = kWaves * 64;
   constexpr int NT = (NH + 15) / 16;  // MFMA tiles of 16 heads
@@ -142,7 +153,8 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeArgs a) {
   // (p * k <= 64 * 2048: 32-bit products and quotients)
   const int lo_full = (p * a.k) / a.P;
   const int n_full = ((p + 1) * a.k) / a.P - lo_full;
-  const int spec_blk = a.topk[(size_t)s * a.k + lo_full + min((int)threadIdx.x, max(n_full - 1, 0))];
+  const int spec_blk =
+      kFusedSel ? 0 : a.topk[(size_t)s * a.k + lo_full + min((int)threadIdx.x, max(n_full - 1, 0))];
 
   const int b = a.sel_req[s];
   const int Lsel = max(a.sel_seq_len[s], 0);
@@ -167,9 +179,15 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeArgs a) {
       bq[nt][kk] = __builtin_bit_cast(bf16x8, real ? v : i32x4{0, 0, 0, 0});
     }
   }
-  // the request and the selecting row's length, fetched while the vector loads
-  // above are in flight (the compiler would otherwise fetch them at first use)
-  asm volatile("" ::"s"(b), "s"(Lsel));
+  SelView sv{nullptr, nullptr, 0};
+  if constexpr (kFusedSel) {
+    sv = select_fn(b);
+  } else {
+    // the request and the selecting row's length, fetched while the vector
+    // loads above are in flight (the compiler would otherwise fetch them at
+    // first use)
+    asm volatile("" ::"s"(b), "s"(Lsel));
+  }
   // longest row of the selection: every row owns some head n < nh
   int tail_hi = 0;
 #pragma unroll
@@ -184,7 +202,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeArgs a) {
   const int nall = nblk + ntailblk;  // blocks of this split (selected, then tail)
   const int page_size = 1 << a.page_log2;
   const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
-  const int32_t* sel = a.topk + (size_t)s * a.k + lo;
+  const int32_t* sel = kFusedSel ? sv.sel + lo : a.topk + (size_t)s * a.k + lo;
 
   float m_run[NT], l_run[NT];
   // O in the MFMA C layout: acc[nt][m][e] = O[head nt*16+4lg+e][d = (D/16) lc + m]
@@ -203,7 +221,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeArgs a) {
     return (((pos >> a.page_log2) * a.Hkv + kvh) << a.page_log2) | (pos & (page_size - 1));
   };
 
-  const bool use_spec = nsel == a.k && n_full <= kThreads;  // then lo == lo_full, nblk == n_full
+  const bool use_spec = !kFusedSel && nsel == a.k && n_full <= kThreads;  // then lo == lo_full, nblk == n_full
   for (int r0 = 0; r0 < nall; r0 += kRound) {
     const int nr = min(kRound, nall - r0);
     // ---- stage block ids and page positions of this round in LDS ----
@@ -217,7 +235,11 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeArgs a) {
       } else {
         tok = tail_lo + 4 * (u - nblk);
       }
-      if (tok >= 0) pos = (bt[tok >> a.page_log2] << a.page_log2) | (tok & (page_size - 1));
+      if (tok >= 0) {
+        const int pg = tok >> a.page_log2;
+        const int pid = (kFusedSel && pg < sv.nbt) ? sv.bt[pg] : bt[pg];
+        pos = (pid << a.page_log2) | (tok & (page_size - 1));
+      }
       blk_tok[i] = tok;
       blk_pos[i] = pos;
     }
@@ -422,6 +444,82 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeArgs a) {
   }
 }
 
+template <int D, int NH, bool FP8, int W>
+__global__ __launch_bounds__(W * 64) void decode_kernel(DecodeArgs a) {
+  decode_body<D, NH, FP8, W, false>(a, [](int) { return SelView{nullptr, nullptr, 0}; });
+}
+
+// ---- selection + attention in one launch ----
+// Every workgroup of selecting row s (all splits and KV heads) runs the
+// row's selection (select_row: the finalize of the scored workspace) into its
+// LDS, then attends.  The selection costs every workgroup the same few
+// microseconds the finalize kernel would take, in parallel; what it saves is
+// the launch boundary, the round trip that reads the selection back and the
+// one that looks up the pages: the request's page-table row is loaded into
+// LDS while the selection runs.  No workgroup waits for another: the row's
+// histogram is only read (the workspace keeps two, and a selection clears the
+// one the next call's scan adds into), and workgroup (0, 0) of each row writes
+// the row's top-k.  One 8-wave workgroup per (split, KV head, row), as the
+// decode.
+constexpr int kBtLds = 4096;        // page-table entries staged in LDS
+constexpr int kFusedMaxTopk = 2048;  // k <= 2048 (checked by the API)
+
+template <int D, int NH>
+constexpr size_t decode_lds_bytes(int W) {
+  constexpr int NHP = ((NH + 15) / 16) * 16;
+  return (size_t)W * 2 * NHP * 4 + (size_t)W * NHP * 4 + (size_t)NHP * (W + 1) * 4 + (size_t)W * NH * D * 4 +
+         2 * (size_t)kRound * 4;
+}
+constexpr size_t kSelectLdsBytes = (kFinThreads / 64) * 4 + kRadixPasses * 256 * 4 + kCandLds * 8 +
+                                   kWordsLds * 8 + 16 + 32 + kMaxChunksPerRow * 2;
+template <int D, int NH>
+constexpr bool select_decode_ok() {
+  return decode_wide_ok<NH>() &&
+         decode_lds_bytes<D, NH>(8) + kSelectLdsBytes + (kFusedMaxTopk + kBtLds) * 4 + 1024 <= 160 * 1024;
+}
+
+template <int D, int NH, bool FP8>
+__global__ __launch_bounds__(kFinThreads) void select_decode_kernel(DecodeArgs a, WsPtrs ws, int32_t max_seq_len,
+                                                                     int32_t* __restrict__ topk_out) {
+  static_assert(kFinThreads == 8 * 64, "the selection runs on the decode's 8 waves");
+  __shared__ int32_t sel_lds[kFusedMaxTopk];
+  __shared__ int32_t bt_lds[kBtLds];
+  constexpr int kBtPer = kBtLds / kFinThreads;
+  const int s = blockIdx.z;
+  const uint32_t t = ws.gen[0];  // the scan's histogram: t & 1
+  auto select = [&](int b) -> SelView {
+    int nbt = 0;
+    int btv[kBtPer];
+    // issued after the selection's first loads, which wait for nothing (the
+    // row length and the request are loaded by then; past nbt the loads
+    // re-read a valid entry and are dropped)
+    auto hook = [&] {
+      const int Lsel = max(a.sel_seq_len[s], 0);
+      const int need = min((int)(((int64_t)Lsel + (1 << a.page_log2) - 1) >> a.page_log2), a.max_pages);
+      nbt = need <= kBtLds ? need : 0;  // longer rows look their pages up in global memory
+      const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
+#pragma unroll
+      for (int i = 0; i < kBtPer; ++i) btv[i] = bt[min((int)threadIdx.x + kFinThreads * i, max(nbt - 1, 0))];
+    };
+    select_row<true, true>(s, a.sel_seq_len, a.k, max_seq_len, nullptr, sel_lds, ws, t, hook);
+#pragma unroll
+    for (int i = 0; i < kBtPer; ++i) {
+      const int e = (int)threadIdx.x + kFinThreads * i;
+      if (e < nbt) bt_lds[e] = btv[i];
+    }
+    return SelView{sel_lds, bt_lds, nbt};  // (the decode's staging barrier publishes both)
+  };
+  decode_body<D, NH, FP8, 8, true>(a, select);
+  // Global writes last: the decode's waits on global memory come in issue
+  // order.  Workgroup (0, 0) of the row writes the row's top-k and clears its
+  // row of the next call's histogram; one workgroup publishes the count.
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int i = threadIdx.x; i < a.k; i += kFinThreads) topk_out[(size_t)s * a.k + i] = sel_lds[i];
+    clear_next_hist(ws, s, t);
+    if (s == 0 && threadIdx.x == 0) ws.gen[1] = t;
+  }
+}
+
 // ---- merge: one wave per (row, head) ----
 // The partials' LSEs and outputs are loaded in one round (16 partials at a
 // time), then reduced: lane p holds lse_p; the outputs are weighted by
@@ -505,13 +603,12 @@ qsa_status launch_decode_nh(int nh, dim3 grid, DecodeArgs a, hipStream_t stream)
 
 }  // namespace
 
-qsa_status launch_sparse_decode(const qsa_config& c, int32_t S, int32_t q_per_sel, int32_t P,
-                                const void* q, const int32_t* row_seq_len, const int32_t* sel_req,
-                                const int32_t* sel_seq_len, const int32_t* topk,
-                                const int32_t* block_table, const void* k_cache,
-                                const void* v_cache, const float* k_scale, const float* v_scale,
-                                float* o_part, float* lse_part, hipStream_t stream) {
-  if (S == 0) return QSA_OK;
+namespace {
+
+DecodeArgs decode_args(const qsa_config& c, int32_t S, int32_t q_per_sel, int32_t P, const void* q,
+                       const int32_t* row_seq_len, const int32_t* sel_req, const int32_t* sel_seq_len,
+                       const int32_t* topk, const int32_t* block_table, const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale, float* o_part, float* lse_part) {
   DecodeArgs a;
   a.q = reinterpret_cast<const uint16_t*>(q);
   a.row_seq_len = row_seq_len;
@@ -536,6 +633,42 @@ qsa_status launch_sparse_decode(const qsa_config& c, int32_t S, int32_t q_per_se
   a.P = P;
   a.R = S * q_per_sel;
   a.scale_log2 = c.softmax_scale * kLog2e;
+  return a;
+}
+
+// false: this shape has no fused kernel (the caller runs the two kernels)
+template <int D, int NH, bool FP8>
+bool launch_select_decode_t(dim3 grid, const DecodeArgs& a, const WsPtrs& ws, int32_t max_seq_len,
+                            int32_t* topk, hipStream_t stream) {
+  if constexpr (select_decode_ok<D, NH>()) {
+    hipLaunchKernelGGL((select_decode_kernel<D, NH, FP8>), grid, dim3(kFinThreads), 0, stream, a, ws, max_seq_len,
+                       topk);
+    return true;
+  } else {
+    return false;
+  }
+}
+
+template <int D, bool FP8>
+bool launch_select_decode_nh(int nh, dim3 grid, const DecodeArgs& a, const WsPtrs& ws, int32_t max_seq_len,
+                             int32_t* topk, hipStream_t stream) {
+  if (nh <= 4) return launch_select_decode_t<D, 4, FP8>(grid, a, ws, max_seq_len, topk, stream);
+  if (nh <= 8) return launch_select_decode_t<D, 8, FP8>(grid, a, ws, max_seq_len, topk, stream);
+  if (nh <= 16) return launch_select_decode_t<D, 16, FP8>(grid, a, ws, max_seq_len, topk, stream);
+  return false;
+}
+
+}  // namespace
+
+qsa_status launch_sparse_decode(const qsa_config& c, int32_t S, int32_t q_per_sel, int32_t P,
+                                const void* q, const int32_t* row_seq_len, const int32_t* sel_req,
+                                const int32_t* sel_seq_len, const int32_t* topk,
+                                const int32_t* block_table, const void* k_cache,
+                                const void* v_cache, const float* k_scale, const float* v_scale,
+                                float* o_part, float* lse_part, hipStream_t stream) {
+  if (S == 0) return QSA_OK;
+  const DecodeArgs a = decode_args(c, S, q_per_sel, P, q, row_seq_len, sel_req, sel_seq_len, topk, block_table,
+                                   k_cache, v_cache, k_scale, v_scale, o_part, lse_part);
   dim3 grid(P, c.num_kv_heads, S);
   const bool fp8 = c.kv_dtype == QSA_KV_FP8_E4M3;
   if (c.head_dim == 128)
@@ -545,6 +678,39 @@ qsa_status launch_sparse_decode(const qsa_config& c, int32_t S, int32_t q_per_se
     return fp8 ? launch_decode_nh<64, true>(a.nh, grid, a, stream)
                : launch_decode_nh<64, false>(a.nh, grid, a, stream);
   return fail(QSA_ERR_UNSUPPORTED, "head_dim %d not built", c.head_dim);
+}
+
+qsa_status launch_select_decode(const qsa_config& c, int32_t S, int32_t q_per_sel, int32_t P, int32_t max_seq_len,
+                                const void* q, const int32_t* row_seq_len, const int32_t* sel_req,
+                                const int32_t* sel_seq_len, const int32_t* block_table, const void* k_cache,
+                                const void* v_cache, const float* k_scale, const float* v_scale, int32_t* topk,
+                                float* o_part, float* lse_part, const TopkWorkspace& lay, void* ws_base,
+                                hipStream_t stream) {
+  if (S == 0) return QSA_OK;
+  if (c.head_dim != 64 && c.head_dim != 128) return fail(QSA_ERR_UNSUPPORTED, "head_dim %d not built", c.head_dim);
+  const DecodeArgs a = decode_args(c, S, q_per_sel, P, q, row_seq_len, sel_req, sel_seq_len, topk, block_table,
+                                   k_cache, v_cache, k_scale, v_scale, o_part, lse_part);
+  const WsPtrs ws = ws_ptrs(lay, ws_base);
+  dim3 grid(P, c.num_kv_heads, S);
+  // One launch when the decode would run 8-wave workgroups (fewer than two
+  // per CU), the rows' bitmaps fit the LDS and the shape has a fused kernel;
+  // otherwise the finalize and the decode, one after the other.
+  const int64_t groups = (int64_t)P * c.num_kv_heads * S;
+  bool done = false;
+  if (groups < kDecodeWideMaxGroups && lay.nb_stride / 64 <= kWordsLds) {
+    const bool fp8 = c.kv_dtype == QSA_KV_FP8_E4M3;
+    if (c.head_dim == 128)
+      done = fp8 ? launch_select_decode_nh<128, true>(a.nh, grid, a, ws, max_seq_len, topk, stream)
+                 : launch_select_decode_nh<128, false>(a.nh, grid, a, ws, max_seq_len, topk, stream);
+    else
+      done = fp8 ? launch_select_decode_nh<64, true>(a.nh, grid, a, ws, max_seq_len, topk, stream)
+                 : launch_select_decode_nh<64, false>(a.nh, grid, a, ws, max_seq_len, topk, stream);
+  }
+  if (done) return check_launch("qsa_select_sparse_decode");
+  qsa_status st = launch_finalize_ws(c, S, sel_seq_len, max_seq_len, topk, lay, ws_base, stream);
+  if (st != QSA_OK) return st;
+  return launch_sparse_decode(c, S, q_per_sel, P, q, row_seq_len, sel_req, sel_seq_len, topk, block_table, k_cache,
+                              v_cache, k_scale, v_scale, o_part, lse_part, stream);
 }
 
 qsa_status launch_merge(int32_t P, int32_t R, int32_t H, int32_t d, const float* o_part,

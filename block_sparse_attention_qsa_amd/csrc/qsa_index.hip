@@ -26,11 +26,13 @@
 //            from its scores); the missing blocks among the bin-T candidates
 //            (usually a few hundred) are picked by a radix select; the bitmap
 //            is emitted in ascending order with a popcount prefix sum and
-//            padded with -1.  It clears the row's histogram, so the workspace
-//            stays clean between calls.
+//            padded with -1.  The workspace holds two histograms: a scan adds
+//            into the one its call count picks, and the selection clears the
+//            other, so the workspace stays clean between calls.
 #include "qsa_append.h"
 #include "qsa_device.h"
 #include "qsa_internal.h"
+#include "qsa_select.h"
 
 namespace qsa {
 
@@ -38,16 +40,6 @@ namespace {
 
 constexpr int kScoreThreads = 512;                     // score kernel
 constexpr int kScoreIters = kScoreChunk / kScoreThreads;
-
-struct WsPtrs {
-  int32_t* scores;
-  uint64_t* keys;
-  uint64_t* bitmap;
-  uint64_t* keys2;
-  uint32_t* hist;
-  uint32_t* cinfo;
-  int32_t nb_stride;
-};
 
 // The append half of qsa_compress_index_topk (unused by the plain scan).
 struct AppendArgs {
@@ -61,61 +53,6 @@ struct AppendArgs {
   int32_t chunks;      // grid columns; grid rows from num_rows on append, one request per workgroup
 };
 
-__device__ __forceinline__ int score_bin(int32_t s) {
-  return (int)(((uint32_t)(s + (1 << 24))) >> kBinShift);
-}
-
-__device__ __forceinline__ uint64_t cand_key(int32_t score, uint32_t j) {
-  return ((uint64_t)((uint32_t)score ^ 0x80000000u) << 32) | (uint64_t)(0xffffffffu - j);
-}
-
-__device__ __forceinline__ int32_t key_score(uint64_t key) {
-  return (int32_t)((uint32_t)(key >> 32) ^ 0x80000000u);
-}
-
-// Block-wide exclusive prefix sum (blockDim.x threads, a multiple of 64).
-// kReuse: end with a barrier, so that sh may be written again right away.
-template <int NT, bool kReuse = true>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh /*[NT/64]*/) {
-  const int l = lane_id(), w = threadIdx.x / 64;
-  const uint32_t inc = wave_incl_scan(v);
-  if (l == 63) sh[w] = inc;
-  __syncthreads();
-  uint32_t off = 0;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) off += (i < w) ? sh[i] : 0u;
-  if (kReuse) __syncthreads();
-  return off + inc - v;
-}
-
-// Threshold bin from a histogram held as per-thread counts (thread t holds
-// bins kBins-1-(kPer t + i), i.e. descending): the bin T with
-// count(bins > T) < ks <= count(bins >= T).  Writes (T, count above T).
-template <int NT>
-__device__ __forceinline__ void threshold_from_counts(const uint32_t (&cnt)[kBins / NT], uint32_t ks,
-                                                      uint32_t* sh, int32_t* s_T, uint32_t* s_above) {
-  constexpr int kPer = kBins / NT;
-  const int tid = threadIdx.x;
-  uint32_t mine = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) mine += cnt[i];
-  // sh is next written after the barrier below
-  uint32_t above = block_excl_scan<NT, false>(mine, sh);
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if (above < ks && above + cnt[i] >= ks) { *s_T = kBins - 1 - (kPer * tid + i); *s_above = above; }
-    above += cnt[i];
-  }
-  __syncthreads();
-}
-
-template <int NT>
-__device__ __forceinline__ void load_hist_desc(const uint32_t* h, uint32_t (&cnt)[kBins / NT]) {
-  constexpr int kPer = kBins / NT;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) cnt[i] = h[kBins - 1 - (kPer * threadIdx.x + i)];
-}
-
 // Chunk candidates.  Every chunk of 1,024 blocks keeps, as 64-bit keys
 // (score, ~index) in its own region of the row's list, all its valid blocks
 // whose bin is at or above its local bin: the bin of its m-th best valid block
@@ -125,18 +62,6 @@ __device__ __forceinline__ void load_hist_desc(const uint32_t* h, uint32_t (&cnt
 // local bin is above T is read again from its scores.  m is sized so that the
 // list usually fits the finalize's first round of loads (local_m).  The local
 // bin is found by one wave walking down from the chunk's highest bin.
-constexpr int kFinKeys = 8;  // candidate keys per finalize thread and round
-
-// Finalize threads per chunk in a round: as many as share the 512 threads, at
-// most kScoreChunk / kFinKeys (a round never reads past a chunk's list region).
-__device__ __forceinline__ int chunk_threads(int nb_stride) {
-  const int nch = min(nb_stride / kScoreChunk, 64);
-  int t = 1;
-  while (t * 2 * nch <= 512 && t * 2 * kFinKeys <= kScoreChunk) t *= 2;
-  return t;
-}
-__device__ __forceinline__ int local_m(int nb_stride) { return chunk_threads(nb_stride) * 4; }
-
 template <int NT, int IT>
 __device__ __forceinline__ void chunk_candidates(const uint32_t* hist, int maxbin, const int32_t (&sc)[IT], int c,
                                                  int nb, int nb_stride, uint64_t* keys, uint32_t* cinfo,
@@ -237,9 +162,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   const int sr = kAppend ? min(s, ap.num_rows - 1) : s;
   const int Lr = sel_seq_len[sr];
   const int b = sel_req[sr];
+  const uint32_t tgen = ws.gen[1] + 1u;  // this call's count; its histogram is tgen & 1
   // Both row loads and the argument pointers in flight together: the compiler
   // would otherwise fetch each only after the exit tests below, one wait each.
-  asm volatile("" ::"s"(Lr), "s"(b), "s"(block_table), "s"(q_index), "s"(ckey), "s"(max_pages),
+  asm volatile("" ::"s"(Lr), "s"(b), "s"(tgen), "s"(block_table), "s"(q_index), "s"(ckey), "s"(max_pages),
                "s"(page_log2), "s"(ws.scores), "s"(ws.hist), "s"(ws.nb_stride));
   if (kAppend) {
     asm volatile("" ::"s"(ap.seq_len_before), "s"(ap.new_cu), "s"(ap.new_keys), "s"(ap.ring), "s"(ap.num_reqs),
@@ -415,7 +341,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   int32_t* srow = ws.scores + (size_t)s * ws.nb_stride;
 #pragma unroll
   for (int it = 0; it < kScoreIters; ++it) srow[c * kScoreChunk + it * kScoreThreads + threadIdx.x] = sc[it];
-  uint32_t* ghist = ws.hist + (size_t)s * kBins;
+  uint32_t* ghist = ws.hist + (size_t)(tgen & 1u) * ws.hist_stride + (size_t)s * kBins;
+  if (threadIdx.x == 0) ws.gen[0] = tgen;  // (every scoring workgroup writes the same count)
   for (int i = threadIdx.x; i < kBins; i += kScoreThreads) {
     const uint32_t h = hist[i];
     if (h) atomicAdd(&ghist[i], h);
@@ -429,260 +356,19 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
                                                &s_lb, &s_cnt);
 }
 
-// Finalize (one workgroup per selecting row): the row's threshold bin T from
-// its histogram; the chunks' candidate lists (one round of loads, issued before
-// the row length is known) are classified: bin > T -> selected (LDS bitmap),
-// bin == T -> threshold candidates; the missing ones among those are picked
-// by an MSB-first radix select, and the bitmap is emitted in ascending order.
-constexpr int kFinThreads = 512;
-constexpr int kCandLds = 4096;   // threshold candidates held in LDS (more: workspace)
-constexpr int kWordsLds = 4096;  // bitmap words held in LDS (rows up to 262,144 blocks)
-
-// kBmLds: the selection bitmap of every row fits the LDS (the host picks it
-// from the workspace's row stride), so no mark or read of it branches on where
-// it lives.
+// Finalize: one workgroup per selecting row (select_row); then the row of the
+// next call's histogram is cleared and the count published.
 template <bool kBmLds>
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     const int32_t* __restrict__ sel_seq_len, int32_t k, int32_t max_seq_len,
     int32_t* __restrict__ topk, WsPtrs ws) {
-  constexpr int kPer = kBins / kFinThreads;
-  __shared__ uint32_t sh[kFinThreads / 64];
-  constexpr int kRadixPasses = (32 + kBinShift + 7) / 8;  // 8-bit digits below the threshold bin
-  __shared__ __align__(16) uint32_t rhist[kRadixPasses][256];
-  __shared__ uint64_t cand[kCandLds];
-  __shared__ uint64_t bml[kBmLds ? kWordsLds : 1];
-  __shared__ int32_t s_T;
-  __shared__ uint32_t s_above, s_n, s_nfb;
-  __shared__ uint16_t s_fb[kMaxChunksPerRow];  // chunks read again from their scores
   const int s = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int nchunks_max = ws.nb_stride / kScoreChunk;
-  const int tpc = chunk_threads(ws.nb_stride);     // threads per chunk in a round
-  const int cpr = kFinThreads / tpc;               // chunks per round
-  const int sub = tid % tpc;
-  uint32_t* ghist = ws.hist + (size_t)s * kBins;
-  const uint32_t* cinfo = ws.cinfo + (size_t)s * nchunks_max;
-  const uint64_t* ckeys = ws.keys + (size_t)s * ws.nb_stride;
-  const int32_t* srow = ws.scores + (size_t)s * ws.nb_stride;
-  uint64_t* gkeys = ws.keys2 + (size_t)s * ws.nb_stride;
-  uint64_t* bm = ws.bitmap + (size_t)s * (ws.nb_stride / 64);
-
-  // First round, before the row length is known (clamped in bounds, masked
-  // below): the row histogram and, for the first cpr chunks, each chunk's
-  // cinfo and the first tpc * kFinKeys keys of its list.
-  uint32_t hc[kPer];
-  load_hist_desc<kFinThreads>(ghist, hc);
-  int cc = min(tid / tpc, nchunks_max - 1);
-  uint32_t ci = cinfo[cc];
-  uint64_t kk[kFinKeys];
-#pragma unroll
-  for (int e = 0; e < kFinKeys; ++e) kk[e] = ckeys[(size_t)cc * kScoreChunk + sub * kFinKeys + e];
-  const int Lr = sel_seq_len[s];
-  // the histogram and the length before the length test below (the keys and
-  // cinfo, loaded after the histogram, are waited for only after the threshold)
-  asm volatile("" ::"s"(Lr));
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) asm volatile("" ::"v"(hc[i]));
-
-  const int L = min(Lr, max_seq_len);
-  const int nb = max(L, 0) >> 2;
-  int32_t* out = topk + (size_t)s * k;
-  if (nb == 0) {  // nothing was scored: the histogram is untouched
-    for (int i = tid; i < k; i += kFinThreads) out[i] = -1;
-    return;
-  }
-  const uint32_t ks = (uint32_t)min(k, nb);
-  const int nchunks = (nb + kScoreChunk - 1) / kScoreChunk;
-  const int nwords = (nb + 63) >> 6;
-  constexpr bool bm_lds = kBmLds;  // then nwords <= nb_stride / 64 <= kWordsLds
-  if (bm_lds) {
-    for (int i = tid; i < nwords; i += kFinThreads) bml[i] = 0;
-  } else {
-    for (int i = tid; i < nwords; i += kFinThreads) bm[i] = 0;
-  }
-  for (int i = tid; i < kRadixPasses * 64; i += kFinThreads)
-    reinterpret_cast<uint4*>(&rhist[0][0])[i] = uint4{0u, 0u, 0u, 0u};
-  if (tid == 0) { s_n = 0; s_T = 0; s_above = 0; s_nfb = 0; }
-  threshold_from_counts<kFinThreads>(hc, ks, sh, &s_T, &s_above);
-  asm volatile("" ::"v"(ci));
-#pragma unroll
-  for (int e = 0; e < kFinKeys; ++e) asm volatile("" ::"v"(kk[e]));
-  const int T = s_T;
-  const uint32_t above = s_above;
-
-  auto mark = [&](uint32_t j) {
-    if (bm_lds) atomicOr(reinterpret_cast<unsigned long long*>(&bml[j >> 6]), 1ull << (j & 63));
-    else atomicOr(reinterpret_cast<unsigned long long*>(&bm[j >> 6]), 1ull << (j & 63));
-  };
-  auto classify = [&](uint64_t key) {
-    const int bin = score_bin(key_score(key));
-    if (bin > T) {
-      mark(0xffffffffu - (uint32_t)(key & 0xffffffffull));
-    } else if (bin == T) {
-      const uint32_t i = atomicAdd(&s_n, 1u);
-      if (i < (uint32_t)kCandLds) cand[i] = key;
-      else gkeys[i] = key;
-    }
-  };
-  for (int c0 = 0; c0 < nchunks; c0 += cpr) {
-    const int c = c0 + tid / tpc;
-    if (c0 > 0) {  // rows of more than cpr chunks: further rounds
-      cc = min(c, nchunks_max - 1);
-      ci = cinfo[cc];
-#pragma unroll
-      for (int e = 0; e < kFinKeys; ++e) kk[e] = ckeys[(size_t)cc * kScoreChunk + sub * kFinKeys + e];
-    }
-    uint32_t at_t = 0;  // which of this thread's first-round keys are threshold candidates
-    if (c < nchunks) {
-      const uint32_t cnt = ci >> 16;
-      const int lb = (int)(ci & 0xffffu);
-      if (lb <= T) {  // the list holds every block of this chunk with bin >= T
-#pragma unroll
-        for (int e = 0; e < kFinKeys; ++e) {
-          const int bin = score_bin(key_score(kk[e]));
-          const bool valid = (uint32_t)(sub * kFinKeys + e) < cnt;
-          if (valid && bin > T) mark(0xffffffffu - (uint32_t)(kk[e] & 0xffffffffull));
-          at_t |= (valid && bin == T) ? 1u << e : 0u;
-        }
-        for (uint32_t i = (uint32_t)(tpc * kFinKeys + sub); i < cnt; i += tpc)
-          classify(ckeys[(size_t)c * kScoreChunk + i]);
-      } else if (sub == 0) {  // local bin above T: bins [T, lb) are not listed; read the chunk's scores below
-        s_fb[atomicAdd(&s_nfb, 1u)] = (uint16_t)c;
-      }
-    }
-    // The first-round threshold candidates are appended with one slot
-    // reservation per wave (a wave prefix sum of the per-thread counts), so no
-    // returning atomic sits between a thread's keys.
-    const uint32_t na = (uint32_t)__builtin_popcount(at_t);
-    const uint32_t incl = wave_incl_scan(na);
-    const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-    if (wtot) {
-      uint32_t base = 0;
-      if (lane_id() == 0) base = atomicAdd(&s_n, wtot);
-      base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-      uint32_t pos = base + incl - na;
-      if (base + wtot <= (uint32_t)kCandLds) {  // the usual case: all in LDS, no branch per key
-#pragma unroll
-        for (int e = 0; e < kFinKeys; ++e) {
-          if (at_t & (1u << e)) cand[pos] = kk[e];
-          pos += (at_t >> e) & 1u;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < kFinKeys; ++e) {
-          if (at_t & (1u << e)) {
-            if (pos < (uint32_t)kCandLds) cand[pos] = kk[e];
-            else gkeys[pos] = kk[e];
-            ++pos;
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();
-  // Chunks whose list may be short, by the whole workgroup, up to kFbChunks at
-  // a time: their scores are loaded in one round and classified.
-  constexpr int kFbChunks = 4;
-  constexpr int kFbIters = kScoreChunk / kFinThreads;
-  const uint32_t nfb = s_nfb;
-  for (uint32_t f0 = 0; f0 < nfb; f0 += kFbChunks) {
-    int32_t fs[kFbChunks][kFbIters];
-    int fc[kFbChunks];
-#pragma unroll
-    for (int q = 0; q < kFbChunks; ++q) {
-      fc[q] = s_fb[min(f0 + q, nfb - 1)];  // past the list: the last chunk again, not classified
-#pragma unroll
-      for (int it = 0; it < kFbIters; ++it) fs[q][it] = srow[fc[q] * kScoreChunk + it * kFinThreads + tid];
-    }
-#pragma unroll
-    for (int q = 0; q < kFbChunks; ++q) {
-#pragma unroll
-      for (int it = 0; it < kFbIters; ++it) {
-        const int j = fc[q] * kScoreChunk + it * kFinThreads + tid;
-        if (f0 + q < nfb && j < nb) classify(cand_key(fs[q][it], (uint32_t)j));
-      }
-    }
-  }
-  if (nfb) __syncthreads();
-  const uint32_t n = s_n;
-  const uint32_t need = ks - above;  // 1 <= need <= n
-  auto key_at = [&](uint32_t i) -> uint64_t { return i < (uint32_t)kCandLds ? cand[i] : gkeys[i]; };
-
-  // MSB-first radix select of the need-th largest threshold candidate by the
-  // whole workgroup.  All candidates share the threshold bin, i.e. key bits
-  // 32 + kBinShift and up, so the first digit is the 8 bits right below (with
-  // ~300 candidates over 256 digits, one pass usually settles it), then 8 bits
-  // at a time down to bit 0.  Each thread holds one candidate in a register
-  // (any beyond the workgroup's size are read again per pass).  Every pass
-  // counts into a histogram of its own, cleared with the bitmap above, so one
-  // barrier per pass suffices: after it every wave reads the same counts and
-  // finds the digit by itself.
-  constexpr uint64_t kBinMask = ~((1ull << (32 + kBinShift)) - 1ull);
-  const uint64_t mine = key_at(min((uint32_t)tid, n - 1));
-  uint64_t prefix = 0, mask = 0;  // (mask 0 keeps every candidate)
-  if (need < n) {
-    const int l = lane_id();
-    mask = kBinMask;
-    prefix = cand[0] & kBinMask;
-    uint32_t rem = need;
-    for (int p = 0, shift = 32 + kBinShift - 8;; ++p, shift = max(shift - 8, 0)) {
-      uint32_t* h = rhist[p];
-      if ((uint32_t)tid < n && (mine & mask) == prefix) atomicAdd(&h[(mine >> shift) & 0xff], 1u);
-      for (uint32_t i = tid + kFinThreads; i < n; i += kFinThreads) {
-        const uint64_t key = key_at(i);
-        if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 0xff], 1u);
-      }
-      __syncthreads();
-      // lane l owns digits 255-4l .. 252-4l (descending)
-      const uint4 hv = *reinterpret_cast<const uint4*>(&h[252 - 4 * l]);
-      const uint32_t cs[4] = {hv.w, hv.z, hv.y, hv.x};
-      const uint32_t tot = cs[0] + cs[1] + cs[2] + cs[3];
-      uint32_t acc = wave_incl_scan(tot) - tot;  // count in larger digits
-      uint32_t dsel = 0, larger = 0, cnt = 0;
-      bool found = false;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (!found && acc < rem && acc + cs[i] >= rem) { found = true; dsel = 255 - 4 * l - i; larger = acc; cnt = cs[i]; }
-        acc += cs[i];
-      }
-      const int src = __ffsll((long long)__ballot(found)) - 1;
-      dsel = (uint32_t)__builtin_amdgcn_readlane((int)dsel, src);
-      larger = (uint32_t)__builtin_amdgcn_readlane((int)larger, src);
-      cnt = (uint32_t)__builtin_amdgcn_readlane((int)cnt, src);
-      rem -= larger;
-      prefix = (prefix & ~(0xffull << shift)) | ((uint64_t)dsel << shift);
-      mask |= 0xffull << shift;
-      if (cnt == rem || shift == 0) break;  // every remaining candidate with this prefix is kept
-    }
-  }
-  if ((uint32_t)tid < n && (mine & mask) >= prefix) mark(0xffffffffu - (uint32_t)(mine & 0xffffffffull));
-  for (uint32_t i = tid + kFinThreads; i < n; i += kFinThreads) {
-    const uint64_t key = key_at(i);
-    if ((key & mask) >= prefix) mark(0xffffffffu - (uint32_t)(key & 0xffffffffull));
-  }
-  __syncthreads();
-
-  // emit ascending block ids: popcount prefix over the bitmap words
-  const int per = (nwords + kFinThreads - 1) / kFinThreads;
-  const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
-  uint32_t cntw = 0;
-  for (int i = w0; i < w1; ++i) cntw += (uint32_t)__popcll(bm_lds ? bml[i] : bm[i]);
-  uint32_t pos = block_excl_scan<kFinThreads, false>(cntw, sh);  // sh is not written again
-  for (int i = w0; i < w1; ++i) {
-    uint64_t m = bm_lds ? bml[i] : bm[i];
-    while (m) {
-      const int bit = __ffsll((long long)m) - 1;
-      m &= m - 1;
-      if (pos < (uint32_t)k) out[pos] = i * 64 + bit;
-      ++pos;
-    }
-  }
-  for (int i = (int)ks + tid; i < k; i += kFinThreads) out[i] = -1;
-  // The row histogram is consumed: clear it for the next call (each thread the
-  // bins it read).  Last, so that no store is outstanding while the phases
-  // above wait for their loads (the wait counter covers stores too).
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) ghist[kBins - 1 - (kPer * tid + i)] = 0;
+  const uint32_t t = ws.gen[0];
+  select_row<kBmLds, false>(s, sel_seq_len, k, max_seq_len, topk + (size_t)s * k, nullptr, ws, t, [] {});
+  // Last, so that no store is outstanding while the phases above wait for
+  // their loads (the wait counter covers stores too).
+  clear_next_hist(ws, s, t);
+  if (s == 0 && threadIdx.x == 0) ws.gen[1] = t;
 }
 
 // ---------------------------------------------------------------------------
@@ -727,6 +413,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_score_kernel(
   const int g = lane >> 4, col = lane & 15;
   const int r_end = row_cu[b + 1];
   const int r0 = row_cu[b] + tile * kPfRows;
+  const uint32_t tgen = ws.gen[1] + 1u;  // this call's count; its histogram is tgen & 1
   if (r0 >= r_end) return;
   // Lane col holds row r0+col: its length (0 past the request's rows).
   const int rc = min(r0 + col, r_end - 1);
@@ -835,11 +522,12 @@ __global__ __launch_bounds__(kPfThreads) void prefill_score_kernel(
     if (col == 15) atomicMax(&s_pmax[4 * g + i], v);
   }
   __syncthreads();
+  if (threadIdx.x == 0) ws.gen[0] = tgen;  // (every scoring workgroup writes the same count)
   for (int i = threadIdx.x; i < kPfRows * kBins / 2; i += kPfThreads) {
     const uint32_t h = hist[i];
     const int m = (2 * i) / kBins, bin = (2 * i) % kBins;
     if (h && r0 + m < r_end) {
-      uint32_t* gh = ws.hist + (size_t)(r0 + m) * kBins + bin;
+      uint32_t* gh = ws.hist + (size_t)(tgen & 1u) * ws.hist_stride + (size_t)(r0 + m) * kBins + bin;
       if (h & 0xffffu) atomicAdd(gh, h & 0xffffu);
       if (h >> 16) atomicAdd(gh + 1, h >> 16);
     }
@@ -916,8 +604,9 @@ TopkWorkspace topk_workspace_layout(int32_t rows, int32_t max_seq_len) {
   w.off_keys = off;   off = al(off + (size_t)rows * w.nb_stride * 8);
   w.off_bitmap = off; off = al(off + (size_t)rows * (w.nb_stride / 64) * 8);
   w.off_keys2 = off;  off = al(off + (size_t)rows * w.nb_stride * 8);
-  w.off_hist = off;   off = al(off + (size_t)rows * kBins * 4);
+  w.off_hist = off;   off = al(off + 2 * (size_t)rows * kBins * 4);
   w.off_cinfo = off;  off = al(off + (size_t)rows * (w.nb_stride / kScoreChunk) * 4);
+  w.off_gen = off;    off = al(off + 2 * 4);
   w.total = off;
   return w;
 }
@@ -933,19 +622,6 @@ qsa_status launch_ws_clear(void* ws, size_t bytes, hipStream_t stream) {
 }
 
 namespace {
-
-WsPtrs ws_ptrs(const TopkWorkspace& lay, void* ws_base) {
-  char* base = reinterpret_cast<char*>(ws_base);
-  WsPtrs ws;
-  ws.scores = reinterpret_cast<int32_t*>(base + lay.off_scores);
-  ws.keys = reinterpret_cast<uint64_t*>(base + lay.off_keys);
-  ws.bitmap = reinterpret_cast<uint64_t*>(base + lay.off_bitmap);
-  ws.keys2 = reinterpret_cast<uint64_t*>(base + lay.off_keys2);
-  ws.hist = reinterpret_cast<uint32_t*>(base + lay.off_hist);
-  ws.cinfo = reinterpret_cast<uint32_t*>(base + lay.off_cinfo);
-  ws.nb_stride = lay.nb_stride;
-  return ws;
-}
 
 template <bool kAppend>
 qsa_status launch_scan(const qsa_config& c, dim3 grid, const int8_t* q_index, const int32_t* sel_req,
@@ -983,6 +659,13 @@ qsa_status launch_finalize(int32_t rows, const int32_t* seq_len, int32_t k, int3
 }
 
 }  // namespace
+
+qsa_status launch_finalize_ws(const qsa_config& c, int32_t rows, const int32_t* seq_len, int32_t max_seq_len,
+                              int32_t* topk, const TopkWorkspace& lay, void* ws_base, hipStream_t stream) {
+  if (rows == 0) return QSA_OK;
+  return launch_finalize(rows, seq_len, c.topk_blocks, max_seq_len, topk, ws_ptrs(lay, ws_base), stream,
+                         "qsa_select_sparse_decode(finalize)");
+}
 
 qsa_status launch_index_topk(const qsa_config& c, int32_t S, int32_t max_seq_len,
                              const int8_t* q_index, const int32_t* sel_req,

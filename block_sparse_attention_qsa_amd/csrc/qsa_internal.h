@@ -23,8 +23,12 @@ struct TopkWorkspace {
   size_t off_keys;     // uint64 [rows][nb_stride]  each chunk's candidate list, in the chunk's region
   size_t off_bitmap;   // uint64 [rows][nb_stride/64]  (rows too long for the finalize's LDS)
   size_t off_keys2;    // uint64 [rows][nb_stride]  threshold candidates beyond the finalize's LDS
-  size_t off_hist;     // uint32 [rows][kBins]  (all zero between selecting calls)
+  size_t off_hist;     // uint32 [2][rows][kBins]  two histograms: a call scores into one while the
+                       // other is clear (see off_gen)
   size_t off_cinfo;    // uint32 [rows][nb_stride/1024]  per chunk: candidate count << 16 | local bin
+  size_t off_gen;      // uint32 [2]  calls scored / calls selected: a scan uses histogram
+                       // (selected + 1) & 1 and publishes that count as scored; the selection
+                       // reads it, clears the other histogram and publishes it as selected
   size_t total;
 };
 
@@ -72,6 +76,18 @@ qsa_status launch_sparse_decode(const qsa_config& c, int32_t S, int32_t q_per_se
                                 const int32_t* block_table, const void* k_cache,
                                 const void* v_cache, const float* k_scale, const float* v_scale,
                                 float* o_part, float* lse_part, hipStream_t stream);
+
+// Selection (finalize of a scored workspace) fused with qsa_sparse_decode.
+qsa_status launch_select_decode(const qsa_config& c, int32_t S, int32_t q_per_sel, int32_t P, int32_t max_seq_len,
+                                const void* q, const int32_t* row_seq_len, const int32_t* sel_req,
+                                const int32_t* sel_seq_len, const int32_t* block_table, const void* k_cache,
+                                const void* v_cache, const float* k_scale, const float* v_scale, int32_t* topk,
+                                float* o_part, float* lse_part, const TopkWorkspace& lay, void* ws_base,
+                                hipStream_t stream);
+
+// The finalize kernel alone (qsa_index_topk's selection step).
+qsa_status launch_finalize_ws(const qsa_config& c, int32_t rows, const int32_t* seq_len, int32_t max_seq_len,
+                              int32_t* topk, const TopkWorkspace& lay, void* ws_base, hipStream_t stream);
 
 qsa_status launch_merge(int32_t P, int32_t R, int32_t H, int32_t d, const float* o_part,
                         const float* lse_part, void* out, bool out_bf16, float* lse, hipStream_t stream);

@@ -1,0 +1,463 @@
+// Row selection from a scored workspace: the finalize step of qsa_index_topk.
+//
+// Method ("Qwen 4 QSA 迎来解码上下文并行" blog, section on what the pull request
+// changes): keep the best 512 micro-blocks of a row; ("PR #53896 完整报告",
+// implementation breakdown / key source snippets) weight-free top-k over the
+// compressed keys, fixed-width int32 output padded with -1.  Ties go to the
+// lower block index.
+//
+// The scan kernels (qsa_index.hip) leave per row: the exact int32 scores, a
+// histogram of the scores' top bits and, per chunk of 1,024 blocks, a candidate
+// list.  select_row turns that into the row's ascending top-k.  It runs in
+// the finalize kernel (one workgroup per row) and, inlined, at the head of the
+// fused selection + attention kernel (qsa_decode.hip), where every workgroup
+// of a row computes the same selection into its LDS.
+#pragma once
+
+#include "qsa_device.h"
+#include "qsa_internal.h"
+
+namespace qsa {
+
+namespace {
+
+struct WsPtrs {
+  int32_t* scores;
+  uint64_t* keys;
+  uint64_t* bitmap;
+  uint64_t* keys2;
+  uint32_t* hist;       // two histograms of rows x kBins, hist_stride apart
+  uint32_t* cinfo;
+  uint32_t* gen;        // [0]: calls scored, [1]: calls selected (see TopkWorkspace)
+  size_t hist_stride;
+  int32_t nb_stride;
+};
+
+inline WsPtrs ws_ptrs(const TopkWorkspace& lay, void* ws_base) {
+  char* base = reinterpret_cast<char*>(ws_base);
+  WsPtrs ws;
+  ws.scores = reinterpret_cast<int32_t*>(base + lay.off_scores);
+  ws.keys = reinterpret_cast<uint64_t*>(base + lay.off_keys);
+  ws.bitmap = reinterpret_cast<uint64_t*>(base + lay.off_bitmap);
+  ws.keys2 = reinterpret_cast<uint64_t*>(base + lay.off_keys2);
+  ws.hist = reinterpret_cast<uint32_t*>(base + lay.off_hist);
+  ws.cinfo = reinterpret_cast<uint32_t*>(base + lay.off_cinfo);
+  ws.gen = reinterpret_cast<uint32_t*>(base + lay.off_gen);
+  ws.hist_stride = (size_t)lay.rows * kBins;
+  ws.nb_stride = lay.nb_stride;
+  return ws;
+}
+
+__device__ __forceinline__ int score_bin(int32_t s) {
+  return (int)(((uint32_t)(s + (1 << 24))) >> kBinShift);
+}
+
+// 64-bit candidate key: larger key = higher score, then lower block index.
+__device__ __forceinline__ uint64_t cand_key(int32_t score, uint32_t j) {
+  return ((uint64_t)((uint32_t)score ^ 0x80000000u) << 32) | (uint64_t)(0xffffffffu - j);
+}
+
+__device__ __forceinline__ int32_t key_score(uint64_t key) {
+  return (int32_t)((uint32_t)(key >> 32) ^ 0x80000000u);
+}
+
+// Block-wide exclusive prefix sum (blockDim.x threads, a multiple of 64).
+// kReuse: end with a barrier, so that sh may be written again right away.
+template <int NT, bool kReuse = true>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh /*[NT/64]*/) {
+  const int l = lane_id(), w = threadIdx.x / 64;
+  const uint32_t inc = wave_incl_scan(v);
+  if (l == 63) sh[w] = inc;
+  __syncthreads();
+  uint32_t off = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) off += (i < w) ? sh[i] : 0u;
+  if (kReuse) __syncthreads();
+  return off + inc - v;
+}
+
+// Threshold bin from a histogram held as per-thread counts (thread t holds
+// bins kBins-1-(kPer t + i), i.e. descending): the bin T with
+// count(bins > T) < ks <= count(bins >= T).  Writes (T, count above T).
+template <int NT>
+__device__ __forceinline__ void threshold_from_counts(const uint32_t (&cnt)[kBins / NT], uint32_t ks,
+                                                      uint32_t* sh, int32_t* s_T, uint32_t* s_above) {
+  constexpr int kPer = kBins / NT;
+  const int tid = threadIdx.x;
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) mine += cnt[i];
+  // sh is next written after the barrier below
+  uint32_t above = block_excl_scan<NT, false>(mine, sh);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (above < ks && above + cnt[i] >= ks) { *s_T = kBins - 1 - (kPer * tid + i); *s_above = above; }
+    above += cnt[i];
+  }
+  __syncthreads();
+}
+
+template <int NT>
+__device__ __forceinline__ void load_hist_desc(const uint32_t* h, uint32_t (&cnt)[kBins / NT]) {
+  constexpr int kPer = kBins / NT;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) cnt[i] = h[kBins - 1 - (kPer * threadIdx.x + i)];
+}
+
+constexpr int kFinKeys = 8;  // candidate keys per finalize thread and round
+
+// Finalize threads per chunk in a round: as many as share the 512 threads, at
+// most kScoreChunk / kFinKeys (a round never reads past a chunk's list region).
+__device__ __forceinline__ int chunk_threads(int nb_stride) {
+  const int nch = min(nb_stride / kScoreChunk, 64);
+  int t = 1;
+  while (t * 2 * nch <= 512 && t * 2 * kFinKeys <= kScoreChunk) t *= 2;
+  return t;
+}
+__device__ __forceinline__ int local_m(int nb_stride) { return chunk_threads(nb_stride) * 4; }
+
+// The digit of an MSB-first radix select from one pass's 256-bin histogram:
+// lane l owns digits 255-4l .. 252-4l (descending).  Picks the digit holding
+// the rem-th largest key; returns the count in larger digits and in the digit.
+__device__ __forceinline__ void radix_digit(const uint32_t* h, uint32_t rem, uint32_t& dsel, uint32_t& larger,
+                                            uint32_t& cnt) {
+  const int l = lane_id();
+  const uint4 hv = *reinterpret_cast<const uint4*>(&h[252 - 4 * l]);
+  const uint32_t cs[4] = {hv.w, hv.z, hv.y, hv.x};
+  const uint32_t tot = cs[0] + cs[1] + cs[2] + cs[3];
+  uint32_t acc = wave_incl_scan(tot) - tot;  // count in larger digits
+  dsel = 0; larger = 0; cnt = 0;
+  bool found = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!found && acc < rem && acc + cs[i] >= rem) { found = true; dsel = 255 - 4 * l - i; larger = acc; cnt = cs[i]; }
+    acc += cs[i];
+  }
+  const int src = __ffsll((long long)__ballot(found)) - 1;
+  dsel = (uint32_t)__builtin_amdgcn_readlane((int)dsel, src);
+  larger = (uint32_t)__builtin_amdgcn_readlane((int)larger, src);
+  cnt = (uint32_t)__builtin_amdgcn_readlane((int)cnt, src);
+}
+
+// Selection of one row, by a workgroup of kFinThreads threads: the row's
+// threshold bin T from its histogram; the chunks' candidate lists (one round
+// of loads, issued before the row length is known) are classified: bin > T ->
+// selected (bitmap), bin == T -> threshold candidates; the missing ones among
+// those are picked by an MSB-first radix select, and the bitmap is emitted in
+// ascending order.
+constexpr int kFinThreads = 512;
+constexpr int kCandLds = 4096;   // threshold candidates held in LDS (more: see below)
+constexpr int kWordsLds = 4096;  // bitmap words held in LDS (rows up to 262,144 blocks)
+constexpr int kRadixPasses = (32 + kBinShift + 7) / 8;  // 8-bit digits below the threshold bin
+
+// kBmLds: the selection bitmap of every row fits the LDS (the host picks it
+// from the workspace's row stride), so no mark or read of it branches on where
+// it lives.
+//
+// t: the workspace's count of scored calls (gen[0]); the scan left the row's
+// histogram in histogram t & 1.  Both rows are loaded (the count arrives with
+// them) and one is used; neither is written.  The caller clears the other
+// histogram for the next scan (clear_next_hist) and publishes t as selected.
+//
+// kFused = false (finalize kernel, one workgroup per row): the result goes to
+// out (global, k entries); candidates beyond kCandLds spill to the workspace.
+// kFused = true (every workgroup of the fused kernel that serves row s): the
+// result goes to sel (LDS, k entries) and, when out is not null, to out too;
+// nothing is written to the workspace.  More than kCandLds threshold
+// candidates (rows of massively tied scores) are not stored: the radix select
+// and the marking then visit them again in the chunk lists and scores.
+// hook() runs once the first round of loads is in flight.
+template <bool kBmLds, bool kFused, class Hook>
+__device__ __forceinline__ void select_row(int s, const int32_t* __restrict__ sel_seq_len, int32_t k,
+                                           int32_t max_seq_len, int32_t* __restrict__ out, int32_t* sel,
+                                           const WsPtrs& ws, uint32_t t, Hook&& hook) {
+  constexpr int kPer = kBins / kFinThreads;
+  __shared__ uint32_t sh[kFinThreads / 64];
+  __shared__ __align__(16) uint32_t rhist[kRadixPasses][256];
+  __shared__ uint64_t cand[kCandLds];
+  __shared__ uint64_t bml[kBmLds ? kWordsLds : 1];
+  __shared__ int32_t s_T;
+  __shared__ uint32_t s_above, s_n, s_nfb;
+  __shared__ uint16_t s_fb[kMaxChunksPerRow];  // chunks read again from their scores
+  const int tid = threadIdx.x;
+  const int nchunks_max = ws.nb_stride / kScoreChunk;
+  const int tpc = chunk_threads(ws.nb_stride);     // threads per chunk in a round
+  const int cpr = kFinThreads / tpc;               // chunks per round
+  const int sub = tid % tpc;
+  const uint32_t* ghist0 = ws.hist + (size_t)s * kBins;  // the row in histogram 0
+  const uint32_t* cinfo = ws.cinfo + (size_t)s * nchunks_max;
+  const uint64_t* ckeys = ws.keys + (size_t)s * ws.nb_stride;
+  const int32_t* srow = ws.scores + (size_t)s * ws.nb_stride;
+  uint64_t* gkeys = ws.keys2 + (size_t)s * ws.nb_stride;
+  uint64_t* bm = ws.bitmap + (size_t)s * (ws.nb_stride / 64);
+
+  // First round, before the row length is known (clamped in bounds, masked
+  // below): the row histogram and, for the first cpr chunks, each chunk's
+  // cinfo and the first tpc * kFinKeys keys of its list.
+  uint32_t h0[kPer], h1[kPer];
+  load_hist_desc<kFinThreads>(ghist0, h0);
+  load_hist_desc<kFinThreads>(ghist0 + ws.hist_stride, h1);
+  int cc = min(tid / tpc, nchunks_max - 1);
+  uint32_t ci = cinfo[cc];
+  uint64_t kk[kFinKeys];
+#pragma unroll
+  for (int e = 0; e < kFinKeys; ++e) kk[e] = ckeys[(size_t)cc * kScoreChunk + sub * kFinKeys + e];
+  const int Lr = sel_seq_len[s];
+  hook();
+  // the histogram and the length before the length test below (the keys and
+  // cinfo, loaded after the histogram, are waited for only after the threshold)
+  asm volatile("" ::"s"(Lr));
+  uint32_t hc[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    asm volatile("" ::"v"(h0[i]), "v"(h1[i]));
+    hc[i] = (t & 1u) ? h1[i] : h0[i];
+  }
+
+  const int L = min(Lr, max_seq_len);
+  const int nb = max(L, 0) >> 2;
+  if (nb == 0) {  // nothing was scored: the histogram is untouched
+    for (int i = tid; i < k; i += kFinThreads) {
+      if (kFused) sel[i] = -1;
+      if (out) out[i] = -1;
+    }
+    return;
+  }
+  const uint32_t ks = (uint32_t)min(k, nb);
+  const int nchunks = (nb + kScoreChunk - 1) / kScoreChunk;
+  const int nwords = (nb + 63) >> 6;
+  constexpr bool bm_lds = kBmLds;  // then nwords <= nb_stride / 64 <= kWordsLds
+  if (bm_lds) {
+    for (int i = tid; i < nwords; i += kFinThreads) bml[i] = 0;
+  } else {
+    for (int i = tid; i < nwords; i += kFinThreads) bm[i] = 0;
+  }
+  for (int i = tid; i < kRadixPasses * 64; i += kFinThreads)
+    reinterpret_cast<uint4*>(&rhist[0][0])[i] = uint4{0u, 0u, 0u, 0u};
+  if (tid == 0) { s_n = 0; s_T = 0; s_above = 0; s_nfb = 0; }
+  threshold_from_counts<kFinThreads>(hc, ks, sh, &s_T, &s_above);
+  asm volatile("" ::"v"(ci));
+#pragma unroll
+  for (int e = 0; e < kFinKeys; ++e) asm volatile("" ::"v"(kk[e]));
+  const int T = s_T;
+  const uint32_t above = s_above;
+
+  auto mark = [&](uint32_t j) {
+    if (bm_lds) atomicOr(reinterpret_cast<unsigned long long*>(&bml[j >> 6]), 1ull << (j & 63));
+    else atomicOr(reinterpret_cast<unsigned long long*>(&bm[j >> 6]), 1ull << (j & 63));
+  };
+  auto keep = [&](uint32_t i, uint64_t key) {
+    if (i < (uint32_t)kCandLds) cand[i] = key;
+    else if (!kFused) gkeys[i] = key;
+  };
+  auto classify = [&](uint64_t key) {
+    const int bin = score_bin(key_score(key));
+    if (bin > T) {
+      mark(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+    } else if (bin == T) {
+      keep(atomicAdd(&s_n, 1u), key);
+    }
+  };
+  for (int c0 = 0; c0 < nchunks; c0 += cpr) {
+    const int c = c0 + tid / tpc;
+    if (c0 > 0) {  // rows of more than cpr chunks: further rounds
+      cc = min(c, nchunks_max - 1);
+      ci = cinfo[cc];
+#pragma unroll
+      for (int e = 0; e < kFinKeys; ++e) kk[e] = ckeys[(size_t)cc * kScoreChunk + sub * kFinKeys + e];
+    }
+    uint32_t at_t = 0;  // which of this thread's first-round keys are threshold candidates
+    if (c < nchunks) {
+      const uint32_t cnt = ci >> 16;
+      const int lb = (int)(ci & 0xffffu);
+      if (lb <= T) {  // the list holds every block of this chunk with bin >= T
+#pragma unroll
+        for (int e = 0; e < kFinKeys; ++e) {
+          const int bin = score_bin(key_score(kk[e]));
+          const bool valid = (uint32_t)(sub * kFinKeys + e) < cnt;
+          if (valid && bin > T) mark(0xffffffffu - (uint32_t)(kk[e] & 0xffffffffull));
+          at_t |= (valid && bin == T) ? 1u << e : 0u;
+        }
+        for (uint32_t i = (uint32_t)(tpc * kFinKeys + sub); i < cnt; i += tpc)
+          classify(ckeys[(size_t)c * kScoreChunk + i]);
+      } else if (sub == 0) {  // local bin above T: bins [T, lb) are not listed; read the chunk's scores below
+        s_fb[atomicAdd(&s_nfb, 1u)] = (uint16_t)c;
+      }
+    }
+    // The first-round threshold candidates are appended with one slot
+    // reservation per wave (a wave prefix sum of the per-thread counts), so no
+    // returning atomic sits between a thread's keys.
+    const uint32_t na = (uint32_t)__builtin_popcount(at_t);
+    const uint32_t incl = wave_incl_scan(na);
+    const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    if (wtot) {
+      uint32_t base = 0;
+      if (lane_id() == 0) base = atomicAdd(&s_n, wtot);
+      base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+      uint32_t pos = base + incl - na;
+      if (base + wtot <= (uint32_t)kCandLds) {  // the usual case: all in LDS, no branch per key
+#pragma unroll
+        for (int e = 0; e < kFinKeys; ++e) {
+          if (at_t & (1u << e)) cand[pos] = kk[e];
+          pos += (at_t >> e) & 1u;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < kFinKeys; ++e) {
+          if (at_t & (1u << e)) {
+            keep(pos, kk[e]);
+            ++pos;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // Chunks whose list may be short, by the whole workgroup, up to kFbChunks at
+  // a time: their scores are loaded in one round and classified.
+  constexpr int kFbChunks = 4;
+  constexpr int kFbIters = kScoreChunk / kFinThreads;
+  const uint32_t nfb = s_nfb;
+  for (uint32_t f0 = 0; f0 < nfb; f0 += kFbChunks) {
+    int32_t fs[kFbChunks][kFbIters];
+    int fc[kFbChunks];
+#pragma unroll
+    for (int q = 0; q < kFbChunks; ++q) {
+      fc[q] = s_fb[min(f0 + q, nfb - 1)];  // past the list: the last chunk again, not classified
+#pragma unroll
+      for (int it = 0; it < kFbIters; ++it) fs[q][it] = srow[fc[q] * kScoreChunk + it * kFinThreads + tid];
+    }
+#pragma unroll
+    for (int q = 0; q < kFbChunks; ++q) {
+#pragma unroll
+      for (int it = 0; it < kFbIters; ++it) {
+        const int j = fc[q] * kScoreChunk + it * kFinThreads + tid;
+        if (f0 + q < nfb && j < nb) classify(cand_key(fs[q][it], (uint32_t)j));
+      }
+    }
+  }
+  if (nfb) __syncthreads();
+  const uint32_t n = s_n;
+  const uint32_t need = ks - above;  // 1 <= need <= n
+  auto key_at = [&](uint32_t i) -> uint64_t { return i < (uint32_t)kCandLds ? cand[i] : gkeys[i]; };
+
+  // MSB-first radix select of the need-th largest threshold candidate by the
+  // whole workgroup.  All candidates share the threshold bin, i.e. key bits
+  // 32 + kBinShift and up, so the first digit is the 8 bits right below (with
+  // ~300 candidates over 256 digits, one pass usually settles it), then 8 bits
+  // at a time down to bit 0.  Each thread holds one candidate in a register
+  // (any beyond the workgroup's size are read again per pass).  Every pass
+  // counts into a histogram of its own, cleared with the bitmap above, so one
+  // barrier per pass suffices: after it every wave reads the same counts and
+  // finds the digit by itself.
+  constexpr uint64_t kBinMask = ~((1ull << (32 + kBinShift)) - 1ull);
+  if (!kFused || n <= (uint32_t)kCandLds) {
+    const uint64_t mine = key_at(min((uint32_t)tid, n - 1));
+    uint64_t prefix = 0, mask = 0;  // (mask 0 keeps every candidate)
+    if (need < n) {
+      mask = kBinMask;
+      prefix = cand[0] & kBinMask;
+      uint32_t rem = need;
+      for (int p = 0, shift = 32 + kBinShift - 8;; ++p, shift = max(shift - 8, 0)) {
+        uint32_t* h = rhist[p];
+        if ((uint32_t)tid < n && (mine & mask) == prefix) atomicAdd(&h[(mine >> shift) & 0xff], 1u);
+        for (uint32_t i = tid + kFinThreads; i < n; i += kFinThreads) {
+          const uint64_t key = key_at(i);
+          if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 0xff], 1u);
+        }
+        __syncthreads();
+        uint32_t dsel, larger, cnt;
+        radix_digit(h, rem, dsel, larger, cnt);
+        rem -= larger;
+        prefix = (prefix & ~(0xffull << shift)) | ((uint64_t)dsel << shift);
+        mask |= 0xffull << shift;
+        if (cnt == rem || shift == 0) break;  // every remaining candidate with this prefix is kept
+      }
+    }
+    if ((uint32_t)tid < n && (mine & mask) >= prefix) mark(0xffffffffu - (uint32_t)(mine & 0xffffffffull));
+    for (uint32_t i = tid + kFinThreads; i < n; i += kFinThreads) {
+      const uint64_t key = key_at(i);
+      if ((key & mask) >= prefix) mark(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+    }
+  } else {
+    // Fused, more candidates than the LDS holds (need <= k < n): every pass
+    // and the marking visit the threshold candidates where the classification
+    // found them, the chunk lists (local bin <= T) and the chunk scores (local
+    // bin above T), with the classification's thread-to-chunk mapping.
+    auto visit = [&](auto&& f) {
+      for (int c0 = 0; c0 < nchunks; c0 += cpr) {
+        const int c = c0 + tid / tpc;
+        if (c >= nchunks) continue;
+        const uint32_t cinf = cinfo[c];
+        if ((int)(cinf & 0xffffu) <= T) {
+          const uint32_t cnt = cinf >> 16;
+          for (uint32_t i = sub; i < cnt; i += tpc) {
+            const uint64_t key = ckeys[(size_t)c * kScoreChunk + i];
+            if (score_bin(key_score(key)) == T) f(key);
+          }
+        } else {
+          const int jn = min(kScoreChunk, nb - c * kScoreChunk);
+          for (int i = sub; i < jn; i += tpc) {
+            const uint32_t j = (uint32_t)(c * kScoreChunk + i);
+            const uint64_t key = cand_key(srow[j], j);
+            if (score_bin(key_score(key)) == T) f(key);
+          }
+        }
+      }
+    };
+    uint64_t mask = kBinMask, prefix = cand[0] & kBinMask;
+    uint32_t rem = need;
+    for (int p = 0, shift = 32 + kBinShift - 8;; ++p, shift = max(shift - 8, 0)) {
+      uint32_t* h = rhist[p];
+      visit([&](uint64_t key) {
+        if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 0xff], 1u);
+      });
+      __syncthreads();
+      uint32_t dsel, larger, cnt;
+      radix_digit(h, rem, dsel, larger, cnt);
+      rem -= larger;
+      prefix = (prefix & ~(0xffull << shift)) | ((uint64_t)dsel << shift);
+      mask |= 0xffull << shift;
+      if (cnt == rem || shift == 0) break;
+    }
+    visit([&](uint64_t key) {
+      if ((key & mask) >= prefix) mark(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+    });
+  }
+  __syncthreads();
+
+  // emit ascending block ids: popcount prefix over the bitmap words
+  const int per = (nwords + kFinThreads - 1) / kFinThreads;
+  const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
+  uint32_t cntw = 0;
+  for (int i = w0; i < w1; ++i) cntw += (uint32_t)__popcll(bm_lds ? bml[i] : bm[i]);
+  uint32_t pos = block_excl_scan<kFinThreads, false>(cntw, sh);  // sh is not written again
+  for (int i = w0; i < w1; ++i) {
+    uint64_t m = bm_lds ? bml[i] : bm[i];
+    while (m) {
+      const int bit = __ffsll((long long)m) - 1;
+      m &= m - 1;
+      if (pos < (uint32_t)k) {
+        if (kFused) sel[pos] = i * 64 + bit;
+        if (out) out[pos] = i * 64 + bit;
+      }
+      ++pos;
+    }
+  }
+  for (int i = (int)ks + tid; i < k; i += kFinThreads) {
+    if (kFused) sel[i] = -1;
+    if (out) out[i] = -1;
+  }
+}
+
+// After the selection of the call counted t: row s of the other histogram,
+// the one the next scan adds into, back to zero (the workgroup's threads share
+// it; the last call that used it finished before this call's scan began).
+__device__ __forceinline__ void clear_next_hist(const WsPtrs& ws, int s, uint32_t t) {
+  uint4* h = reinterpret_cast<uint4*>(ws.hist + (size_t)((t + 1u) & 1u) * ws.hist_stride + (size_t)s * kBins);
+  for (int i = threadIdx.x; i < kBins / 4; i += blockDim.x) h[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+}  // namespace
+
+}  // namespace qsa

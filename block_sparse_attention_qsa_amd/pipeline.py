@@ -6,7 +6,9 @@ top-k workspace, selection, split partials, output) for a Workload, and runs
     compress  ->  index_topk  ->  sparse_decode  ->  merge_partials
 
 on one stream; when the step appends at most 5 tokens per request the first
-two are one call, qsa_compress_index_topk (fuse_append=False keeps them apart).
+two are one call, qsa_compress_index_topk (fuse_append=False keeps them apart),
+and the selection step of index_topk runs with the attention, in
+qsa_select_sparse_decode (select_decode=False keeps them apart).
 It only allocates and sequences; all arithmetic is in libqsa.so.
 """
 from __future__ import annotations
@@ -46,7 +48,7 @@ def _rows(keys: torch.Tensor, key_off: np.ndarray, lo: np.ndarray, hi: np.ndarra
 class QSALayer:
     def __init__(self, wl: Workload, num_splits: int = 1, poison: bool = False,
                  max_seq_len: Optional[int] = None, out_dtype: torch.dtype = torch.float32,
-                 fuse_append: bool = True):
+                 fuse_append: bool = True, select_decode: bool = True):
         dev = wl.q.device
         self.wl = wl
         self.cfg = config_for(wl)
@@ -74,6 +76,7 @@ class QSALayer:
         self.step_before = torch.as_tensor(wl.prefix_len.astype(np.int32), device=dev)
         self.step_max_new = int((wl.final_len - wl.prefix_len).max()) if B else 0
         self.fused = bool(fuse_append) and self.step_max_new <= 5
+        self.select_decode = bool(select_decode)
 
     def prefill(self, chunk: Optional[int] = None) -> None:
         """Bulk-compress every request's prefix [0, prefix_len) (optionally in chunks)."""
@@ -94,16 +97,18 @@ class QSALayer:
         api.qsa_compress(self.cfg, self.step_keys, self.step_cu, self.step_before, self.wl.block_table,
                          self.ring, self.ckey, self.step_max_new, stream=stream)
 
-    def index(self, stream=None) -> None:
+    def index(self, stream=None, select: bool = True) -> None:
+        """select=False scores only (the selection is left to select_attend)."""
         wl = self.wl
         api.qsa_index_topk(self.cfg, wl.q_index, wl.sel_req, wl.sel_seq_len, wl.block_table, self.ckey,
-                           self.topk, self.workspace, self.max_seq_len, stream=stream)
+                           self.topk if select else None, self.workspace, self.max_seq_len, stream=stream)
 
-    def compress_index(self, stream=None) -> None:
+    def compress_index(self, stream=None, select: bool = True) -> None:
         wl = self.wl
         api.qsa_compress_index_topk(self.cfg, self.step_keys, self.step_cu, self.step_before, self.ring,
-                                    wl.q_index, wl.sel_req, wl.sel_seq_len, wl.block_table, self.ckey, self.topk,
-                                    self.workspace, self.step_max_new, self.max_seq_len, stream=stream)
+                                    wl.q_index, wl.sel_req, wl.sel_seq_len, wl.block_table, self.ckey,
+                                    self.topk if select else None, self.workspace, self.step_max_new,
+                                    self.max_seq_len, stream=stream)
 
     def decode(self, stream=None) -> None:
         wl = self.wl
@@ -111,17 +116,29 @@ class QSALayer:
                               wl.block_table, wl.k_cache, wl.v_cache, self.o_part, self.lse_part,
                               q_per_sel=wl.q_per_sel, k_scale=wl.k_scale, v_scale=wl.v_scale, stream=stream)
 
+    def select_attend(self, stream=None) -> None:
+        """Selection of the scored workspace into topk, then the attention (one call)."""
+        wl = self.wl
+        api.qsa_select_sparse_decode(self.cfg, wl.q, wl.row_seq_len, wl.sel_req, wl.sel_seq_len, wl.block_table,
+                                     wl.k_cache, wl.v_cache, self.topk, self.o_part, self.lse_part,
+                                     self.workspace, self.max_seq_len, q_per_sel=wl.q_per_sel,
+                                     k_scale=wl.k_scale, v_scale=wl.v_scale, stream=stream)
+
     def merge(self, stream=None) -> None:
         api.qsa_merge_partials(self.o_part, self.lse_part, self.out, self.lse, stream=stream)
 
     def step(self, stream=None) -> None:
         """One decode step: the whole hot path."""
+        sel = not self.select_decode
         if self.fused:
-            self.compress_index(stream)
+            self.compress_index(stream, select=sel)
         else:
             self.compress(stream)
-            self.index(stream)
-        self.decode(stream)
+            self.index(stream, select=sel)
+        if self.select_decode:
+            self.select_attend(stream)
+        else:
+            self.decode(stream)
         self.merge(stream)
 
 
@@ -131,14 +148,16 @@ class QSAPrefill(QSALayer):
     attend with qsa_sparse_decode (one selecting row per query row), merge."""
 
     def __init__(self, wl: Workload, num_splits: int = 1, poison: bool = False,
-                 max_seq_len: Optional[int] = None, out_dtype: torch.dtype = torch.float32):
+                 max_seq_len: Optional[int] = None, out_dtype: torch.dtype = torch.float32,
+                 select_decode: bool = True):
         super().__init__(wl, num_splits=num_splits, poison=poison, max_seq_len=max_seq_len, out_dtype=out_dtype,
-                         fuse_append=False)
+                         fuse_append=False, select_decode=select_decode)
         self.row_cu = wl.extra["row_cu"]
         self.max_rows = int(wl.extra["max_rows_per_req"])
 
-    def index(self, stream=None) -> None:
+    def index(self, stream=None, select: bool = True) -> None:
         wl = self.wl
         api.qsa_prefill_index_topk(self.cfg, wl.q_index, self.row_cu, wl.row_seq_len, wl.block_table, self.ckey,
-                                   self.topk, self.workspace, self.max_seq_len, self.max_rows, stream=stream)
+                                   self.topk if select else None, self.workspace, self.max_seq_len, self.max_rows,
+                                   stream=stream)
 

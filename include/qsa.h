@@ -134,9 +134,11 @@ qsa_status qsa_compress(const qsa_config* cfg, int32_t num_reqs, int32_t max_new
 /*
  * Workspace of qsa_index_topk for num_sel_rows rows of context <= max_seq_len.
  * Returns 0 on a bad argument.  Before its FIRST use a workspace must be
- * cleared with qsa_index_topk_workspace_init(); every qsa_index_topk call that
- * selects (topk != NULL) leaves its counters cleared again, so later calls need
- * no clearing.
+ * cleared with qsa_index_topk_workspace_init(), and again before it serves
+ * calls with another num_sel_rows or max_seq_len (its layout follows them).
+ * Every call that selects (an index call with topk != NULL, or
+ * qsa_select_sparse_decode after a scoring call) leaves it ready for the next
+ * call, so later calls need no clearing.
  */
 size_t qsa_index_topk_workspace_size(const qsa_config* cfg, int32_t num_sel_rows,
                                      int32_t max_seq_len);
@@ -162,9 +164,9 @@ qsa_status qsa_index_topk_workspace_init(void* workspace, size_t ws_bytes, hipSt
  *                num_sel_rows * nb_stride * 4 bytes of the workspace
  *                (row s, block j at int32 index s * nb_stride + j, nb_stride =
  *                max_seq_len/4 rounded up to a multiple of 1024).  Nothing is
- *                selected, and the histogram counters stay set: the next call
- *                with topk != NULL on this workspace needs
- *                qsa_index_topk_workspace_init() first.
+ *                selected, and the histogram counters stay set: the workspace
+ *                is then ready for qsa_select_sparse_decode only; any other
+ *                call on it needs qsa_index_topk_workspace_init() first.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (index_dim), WORKSPACE, HIP.
  */
 qsa_status qsa_index_topk(const qsa_config* cfg, int32_t num_sel_rows, int32_t max_seq_len,
@@ -267,6 +269,38 @@ qsa_status qsa_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_
                              const void* k_cache, const void* v_cache,
                              const float* k_scale, const float* v_scale,
                              float* o_part, float* lse_part, hipStream_t stream);
+
+/*
+ * qsa_select_sparse_decode -- the selection step of qsa_index_topk and
+ * qsa_sparse_decode on its result, in one call ([QSA-DCP]: keep the best 512
+ * blocks, then softmax and value aggregation over the kept positions, as
+ * context-parallel partials).  Its outputs are exactly those of
+ *   qsa_index_topk(..., topk, workspace, ...)   (the selection half), then
+ *   qsa_sparse_decode(cfg, num_sel_rows, q_per_sel, num_splits, ..., topk, ...)
+ * on a workspace left by a scoring call with topk == NULL (qsa_index_topk,
+ * qsa_compress_index_topk or qsa_prefill_index_topk) for the same
+ * num_sel_rows, max_seq_len and sel_seq_len; topk (int32 [S, k]) is written as
+ * that selection would write it.  The workspace is left clean (as after a
+ * selecting call).  When the decode would run fewer than two workgroups per CU
+ * (num_splits * H_kv * num_sel_rows < 512), max_seq_len <= 1,048,576 and
+ * q_per_sel * H_q / H_kv <= 16 (<= 8 for head_dim 128), one kernel does both:
+ * every workgroup selects its row itself, so the attention starts without a
+ * launch boundary or a round trip for the selection.  Otherwise the two
+ * kernels run one after the other.
+ *   Arguments as in the two calls: workspace from
+ *   qsa_index_topk_workspace_size(cfg, num_sel_rows, max_seq_len); topk is
+ *   required.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (index_dim, head_dim, group size),
+ *         WORKSPACE, HIP.
+ */
+qsa_status qsa_select_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_t q_per_sel,
+                                    int32_t num_splits, int32_t max_seq_len, const void* q,
+                                    const int32_t* row_seq_len, const int32_t* sel_req,
+                                    const int32_t* sel_seq_len, const int32_t* block_table,
+                                    const void* k_cache, const void* v_cache,
+                                    const float* k_scale, const float* v_scale, int32_t* topk,
+                                    float* o_part, float* lse_part,
+                                    void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * qsa_merge_partials -- log-sum-exp merge of the split partials ([QSA-DCP]:

@@ -144,6 +144,28 @@ def test_decode_rejects(lib):
     assert decode(lib, cfg(), S=0) == 0
 
 
+def test_select_sparse_decode_rejects(lib):
+    c = cfg()
+    n = lib.qsa_index_topk_workspace_size(ctypes.byref(c), 4, 65536)
+
+    def sd(c=c, S=4, qps=1, P=2, L=65536, ws=FAKE, nbytes=n, topk=FAKE, q=FAKE, ks=None, vs=None):
+        return lib.qsa_select_sparse_decode(ctypes.byref(c), S, qps, P, L, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            ks, vs, topk, FAKE, FAKE, ws, nbytes, None)
+    assert sd(c=cfg(index_dim=96)) == 2             # the selection's config check
+    assert sd(c=cfg(head_dim=96)) == 2              # the attention's
+    assert sd(c=cfg(num_q_heads=15)) == 1
+    assert sd(L=_lib.QSA_MAX_SEQ_LEN + 4) == 1
+    assert sd(P=0) == 1
+    assert sd(qps=9) == 2
+    assert sd(topk=None) == 1                       # the selection is an output here
+    assert sd(q=None) == 1
+    assert sd(c=cfg(kv_dtype=1)) == 1               # fp8 without scales
+    assert sd(nbytes=n - 1) == 3
+    assert sd(ws=None) == 3
+    assert sd(ws=ctypes.c_void_p(0x10010)) == 3
+    assert sd(S=0) == 0
+
+
 def test_merge_rejects(lib):
     assert lib.qsa_merge_partials(0, 4, 16, 128, FAKE, FAKE, FAKE, 0, FAKE, None) == 1
     assert lib.qsa_merge_partials(65, 4, 16, 128, FAKE, FAKE, FAKE, 0, FAKE, None) == 1
