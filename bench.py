@@ -239,8 +239,10 @@ def measured_traffic(fused: bool):
         kv = dict(line.split(" = ", 1) for line in open(path).read().splitlines() if " = " in line)
         if kv.get("variant", "separate").strip() != ("fused" if fused else "separate"):
             return None
-        src = os.path.join(ROOT, kv["kernel_source"].strip())
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["kernel_source_sha256"].strip():
+        h = hashlib.sha256()
+        for name in kv["kernel_sources"].split(","):  # the scan kernel's file and the headers it includes
+            h.update(open(os.path.join(ROOT, name.strip()), "rb").read())
+        if h.hexdigest() != kv["kernel_sources_sha256"].strip():
             return None
         return float(kv["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
