@@ -122,8 +122,9 @@ struct SelView {
 };
 
 // The attention of one workgroup (split p, KV head kvh, selecting row s).
-// kFusedSel: the selection is not read from a.topk; select_fn(b) computes it
-// once the workgroup's own loads are in flight and returns where it is.
+// kFusedSel: the selection is not read from a.topk; select_fn(b, load_q)
+// computes it, calls load_q() once its own first loads are in flight, and
+// returns where the selection is.
 template <int D, int NH, bool FP8, int W, bool kFusedSel, class SelectFn>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a, SelectFn&& select_fn) {
   constexpr int kWaves = W;
@@ -160,29 +161,33 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, SelectFn&& sele
   const int Lsel = max(a.sel_seq_len[s], 0);
   // Q as the QK MFMA B operand: lane (lc, lg) holds head n = nt*16+lc, dims
   // 32kk+8lg..+8.  The loads are unconditional (padding heads read the group's
-  // first head and are zeroed), so they all go out with the loads above.
+  // first head and are zeroed), so they all go out with the loads above (with
+  // kFusedSel, after the selection's first loads: those are waited for first).
   bf16x8 bq[NT][KK];
   int rlen[NT];  // context length of the row owning head nt*16+lc
+  auto load_q = [&] {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int n = nt * 16 + lc;
-    const bool real = n < a.nh;
-    const int nn = real ? n : 0;
-    const int i = nn / a.G;
-    const int h = kvh * a.G + (nn - i * a.G);
-    const uint16_t* qrow = a.q + ((size_t)(s * a.qps + i) * a.Hq + h) * D;
-    const int rl = a.row_seq_len[s * a.qps + i];
-    rlen[nt] = real ? rl : -1;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = nt * 16 + lc;
+      const bool real = n < a.nh;
+      const int nn = real ? n : 0;
+      const int i = nn / a.G;
+      const int h = kvh * a.G + (nn - i * a.G);
+      const uint16_t* qrow = a.q + ((size_t)(s * a.qps + i) * a.Hq + h) * D;
+      const int rl = a.row_seq_len[s * a.qps + i];
+      rlen[nt] = real ? rl : -1;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const i32x4 v = ld16(qrow + 32 * kk + 8 * lg);
-      bq[nt][kk] = __builtin_bit_cast(bf16x8, real ? v : i32x4{0, 0, 0, 0});
+      for (int kk = 0; kk < KK; ++kk) {
+        const i32x4 v = ld16(qrow + 32 * kk + 8 * lg);
+        bq[nt][kk] = __builtin_bit_cast(bf16x8, real ? v : i32x4{0, 0, 0, 0});
+      }
     }
-  }
+  };
   SelView sv{nullptr, nullptr, 0};
   if constexpr (kFusedSel) {
-    sv = select_fn(b);
+    sv = select_fn(b, load_q);
   } else {
+    load_q();
     // the request and the selecting row's length, fetched while the vector
     // loads above are in flight (the compiler would otherwise fetch them at
     // first use)
@@ -446,7 +451,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, SelectFn&& sele
 
 template <int D, int NH, bool FP8, int W>
 __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeArgs a) {
-  decode_body<D, NH, FP8, W, false>(a, [](int) { return SelView{nullptr, nullptr, 0}; });
+  decode_body<D, NH, FP8, W, false>(a, [](int, auto&&) { return SelView{nullptr, nullptr, 0}; });
 }
 
 // ---- selection + attention in one launch ----
@@ -487,12 +492,12 @@ __global__ __launch_bounds__(kFinThreads) void select_decode_kernel(DecodeArgs a
   constexpr int kBtPer = kBtLds / kFinThreads;
   const int s = blockIdx.z;
   const uint32_t t = ws.gen[0];  // the scan's histogram: t & 1
-  auto select = [&](int b) -> SelView {
+  auto select = [&](int b, auto&& load_q) -> SelView {
     int nbt = 0;
     int btv[kBtPer];
     // issued after the selection's first loads, which wait for nothing (the
     // row length and the request are loaded by then; past nbt the loads
-    // re-read a valid entry and are dropped)
+    // re-read a valid entry and are dropped); then the attention's own loads
     auto hook = [&] {
       const int Lsel = max(a.sel_seq_len[s], 0);
       const int need = min((int)(((int64_t)Lsel + (1 << a.page_log2) - 1) >> a.page_log2), a.max_pages);
@@ -500,6 +505,7 @@ __global__ __launch_bounds__(kFinThreads) void select_decode_kernel(DecodeArgs a
       const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
 #pragma unroll
       for (int i = 0; i < kBtPer; ++i) btv[i] = bt[min((int)threadIdx.x + kFinThreads * i, max(nbt - 1, 0))];
+      load_q();  // the attention's q and row lengths, needed only after the selection
     };
     select_row<true, true>(s, a.sel_seq_len, a.k, max_seq_len, nullptr, sel_lds, ws, t, hook);
 #pragma unroll

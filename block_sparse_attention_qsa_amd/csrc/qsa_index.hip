@@ -19,7 +19,9 @@
 //            histogram with device-scope atomics, and from that LDS histogram
 //            writes the chunk's candidate list (every block at or above the
 //            bin of its m-th best block; see chunk_candidates).
-//   finalize (one workgroup per selecting row): the row's threshold bin T
+//   finalize (select_row in qsa_select.h: one workgroup per selecting row
+//            here; qsa_select_sparse_decode runs it inside its attention
+//            kernel instead): the row's threshold bin T
 //            (fewer than k scores above T, at least k at or above it) from the
 //            row histogram; the chunks' lists, loaded in one round, are
 //            classified against T (a chunk whose list may be short is re-read
