@@ -132,3 +132,18 @@ def test_select_decode_named_decode_batch():
     a, b = _pair(wl, 4)
     check_layer(wl, a)
     _same(a, b)
+
+
+def test_select_decode_rows_beyond_the_lds_bitmap():
+    """max_seq_len above 1,048,576 tokens: the selection keeps its bitmap in the
+    workspace (rows of up to 4M blocks), and the call takes the two-launch path."""
+    wl = make_workload(SHAPE_MAIN, [70001, 9000, 13], seed=44, device=DEV, name="seldec-bigrows")
+    a = QSALayer(wl, 4, poison=True, max_seq_len=1_200_000)
+    b = QSALayer(wl, 4, poison=True, max_seq_len=1_200_000, select_decode=False)
+    for layer in (a, b):
+        layer.prefill()
+        layer.step()
+        layer.step()          # twice: the workspace protocol across calls
+    torch.cuda.synchronize()
+    check_layer(wl, a)
+    _same(a, b)
