@@ -51,6 +51,9 @@ CASES = [
     ("d64-g8-qps2", QSAShape(16, 2, 64, 128, 64, 32), [12000, 777], 2, 5, 405),
     ("fp8", SHAPE_FP8, [50000, 1234, 9], 1, 8, 406),
     ("k7-short", QSAShape(8, 2, 64, 32, 7, 16), [3, 17, 27, 28, 29, 100, 1000], 1, 2, 407),
+    ("fp8-d64-qps2", QSAShape(16, 2, 64, 64, 512, 64, kv_dtype="fp8"), [30000, 4099, 2], 2, 4, 408),
+    ("page128", QSAShape(16, 2, 128, 64, 512, 128), [50001, 777, 12345], 1, 8, 409),
+    ("k2048", QSAShape(16, 2, 128, 64, 2048, 64), [20000, 9003, 5000], 1, 4, 410),   # the largest k
 ]
 
 
