@@ -24,9 +24,9 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _pair(wl, P, cls=QSALayer):
-    a = cls(wl, P, poison=True)
-    b = cls(wl, P, poison=True, select_decode=False)
+def _pair(wl, P, cls=QSALayer, **kw):
+    a = cls(wl, P, poison=True, **kw)
+    b = cls(wl, P, poison=True, select_decode=False, **kw)
     assert a.select_decode and not b.select_decode
     for layer in (a, b):
         layer.prefill()
@@ -54,6 +54,8 @@ CASES = [
     ("fp8-d64-qps2", QSAShape(16, 2, 64, 64, 512, 64, kv_dtype="fp8"), [30000, 4099, 2], 2, 4, 408),
     ("page128", QSAShape(16, 2, 128, 64, 512, 128), [50001, 777, 12345], 1, 8, 409),
     ("k2048", QSAShape(16, 2, 128, 64, 2048, 64), [20000, 9003, 5000], 1, 4, 410),   # the largest k
+    ("p1", SHAPE_MAIN, [40000, 3001, 2], 1, 1, 411),          # one split
+    ("p32", SHAPE_MAIN, [90001, 20000, 7, 64], 1, 32, 412),   # 32 splits (two rounds of the merge's loads)
 ]
 
 
@@ -150,3 +152,16 @@ def test_select_decode_rows_beyond_the_lds_bitmap():
     torch.cuda.synchronize()
     check_layer(wl, a)
     _same(a, b)
+
+
+def test_select_decode_bf16_out():
+    """bf16 merged output: the fp32 merge rounded to nearest even (torch's cast)."""
+    wl = make_workload(SHAPE_MAIN, [50000, 8191, 600], seed=413, device=DEV, name="seldec-bf16")
+    a, b = _pair(wl, 8, out_dtype=torch.bfloat16)
+    f = QSALayer(wl, 8, poison=True)
+    f.prefill()
+    f.step()
+    torch.cuda.synchronize()
+    check_layer(wl, f)
+    _same(a, b)
+    assert torch.equal(a.out, f.out.to(torch.bfloat16)) and torch.equal(a.lse, f.lse)
