@@ -425,7 +425,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures the one-GPU path only: this build has no multi-GPU mode "
+        print("bench.py measures the one-GPU path only: the library has no multi-GPU mode "
               "(context-parallel sharding is described in the design notes, not built). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)

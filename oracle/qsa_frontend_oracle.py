@@ -10,7 +10,7 @@ projects Q and K from the hidden states (a replicated projection), normalises
 them with a Gemma-style RMSNorm and applies a 1-D rotary position embedding
 (apply_qsa_rmsnorm, apply_qsa_rope), then writes the token K into the raw-key
 ring and selects with Q.  The pages name these steps but print none of their
-formulas, dimensions or the quantisation of this build's int8 indexer; the
+formulas, dimensions or the quantisation of this library's int8 indexer; the
 readings taken (and listed in the design notes):
 
   F1  projection: q = h W_q^T, k = h W_k^T with one weight w_qk [2D, H] (rows
