@@ -56,6 +56,8 @@ CASES = [
     ("k2048", QSAShape(16, 2, 128, 64, 2048, 64), [20000, 9003, 5000], 1, 4, 410),   # the largest k
     ("p1", SHAPE_MAIN, [40000, 3001, 2], 1, 1, 411),          # one split
     ("p32", SHAPE_MAIN, [90001, 20000, 7, 64], 1, 32, 412),   # 32 splits (two rounds of the merge's loads)
+    # 16-token pages: row 0 spans 5,001 pages, more than the LDS page-table copy (looked up in global memory)
+    ("page16-long", QSAShape(16, 2, 128, 64, 512, 16), [80001, 5000, 65536], 1, 4, 414),
 ]
 
 
