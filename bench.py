@@ -229,6 +229,46 @@ def stream_ceiling(stream, reps: int = 10):
             "bytes": nbytes, "GBps": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
 
 
+def stream_at_size(stream, nbytes: int, nbuf: int, iters: int):
+    """The same streaming loads over a transfer of `nbytes` (rounded down to the kernel's tile):
+    `nbuf` buffers read one after another by single-pass launches captured in a graph (so each
+    launch reads cold data, as the scan's rotating layers do), replayed `iters` times, HIP events."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_attention_qsa_amd", "libqsa_ceiling.so"))
+    lib.qsa_stream_tile.restype = ctypes.c_size_t
+    lib.qsa_stream_granule.restype = ctypes.c_size_t
+    lib.qsa_stream_sink_bytes.restype = ctypes.c_size_t
+    lib.qsa_stream_read_once.restype = ctypes.c_int
+    lib.qsa_stream_read_once.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    tile = lib.qsa_stream_tile()
+    n = min(max(1, nbytes // tile) * tile, lib.qsa_stream_granule())
+    bufs = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    sink = torch.empty(lib.qsa_stream_sink_bytes(), dtype=torch.uint8, device="cuda")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for b in bufs:
+            assert lib.qsa_stream_read_once(ctypes.c_void_p(b.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()), sp) == 0
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        a.record(stream)
+        for _ in range(iters):
+            g.replay()
+        e.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(e) * 1e3 / (iters * nbuf)
+    del g, bufs
+    return {"kernel": f"the same loads, one pass over {n} bytes ({n // tile} workgroups), "
+                      f"{nbuf} buffers in rotation, graph-replayed",
+            "bytes": n, "avg_launch_us": us, "GBps": n / (us * 1e-6) / 1e9, "frac_of_peak": n / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
 def measured_traffic(fused: bool):
     """HBM bytes per scan launch from the committed rocprofv3 counter summary,
     or None when the kernel source has changed since the counters were taken
@@ -582,6 +622,11 @@ def main():
                      "launches_timed": n_launches},
     }
     res["stream_ceiling"] = stream_ceiling(stream)
+    if args.kernel_iters > 0:
+        # a bare stream of the scan's size: the rate a transfer this short reaches at all
+        same = stream_at_size(stream, int(scan_per_launch), len(layers), args.kernel_iters)
+        same["scan_frac_of_it"] = res["roofline"]["achieved"] / same["GBps"]
+        res["stream_ceiling"]["at_scan_size"] = same
     if not args.no_cpu_baseline:
         procs = max(1, min(16, os.cpu_count() or 1))
         print(f"[bench] cpu baseline (oracle), one core then {procs} processes ...", file=sys.stderr, flush=True)

@@ -56,4 +56,20 @@ int qsa_stream_read(const void* buf, size_t bytes, void* sink, hipStream_t strea
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
+// One pass of the same loads over a shorter buffer: `bytes` (a multiple of
+// qsa_stream_tile(), at most qsa_stream_granule()) from `buf`, one workgroup
+// per qsa_stream_tile() bytes (eight 16-byte loads per thread), so that a
+// transfer of a kernel's size is timed with the same launch ramp as that
+// kernel.  Returns 0, 1 on a bad argument, 4 on a launch error.
+size_t qsa_stream_tile(void) { return kIterBytes; }
+
+int qsa_stream_read_once(const void* buf, size_t bytes, void* sink, hipStream_t stream) {
+  if (!buf || !sink || bytes == 0 || bytes % kIterBytes != 0 || bytes > kIterBytes * kBlocks ||
+      (reinterpret_cast<uintptr_t>(buf) & 15) != 0)
+    return 1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)(bytes / kIterBytes)), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const i32x4*>(buf), (size_t)1, reinterpret_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
 }  // extern "C"
