@@ -38,7 +38,7 @@ if ROOT not in sys.path:
 
 METRIC = "QSA decode query-rows/s at 256k ctx; achieved HBM GB/s vs MI355X peak"
 HBM_PEAK_GBS = 8000.0
-BENCH_SPLITS = {1: 1, 2: 4, 3: 16, 4: 1, 5: 32}
+BENCH_SPLITS = {1: 1, 2: 4, 3: 16, 4: 1, 5: 8}
 DESCR = {
     1: "tiny: B=1, H 4/1, d=64, L=1,024, top-32 blocks, D=32, contiguous cache, bf16 K/V",
     2: "decode-32k: B=32, H 16/2, d=128, L=32,768, top-512 blocks, D=64, 64-token pages, bf16 K/V",

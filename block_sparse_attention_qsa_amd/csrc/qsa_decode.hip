@@ -76,6 +76,7 @@ struct DecodeArgs {
   float* o_part;
   float* lse_part;
   int32_t k, max_pages, page_log2, Hq, Hkv, G, qps, nh, P, R;
+  int32_t qg, qpw;  // query-row groups per KV head (grid y = Hkv * qg), rows per group (nh = G * qpw)
   float scale_log2;  // softmax_scale * log2(e)
 };
 
@@ -121,7 +122,8 @@ struct SelView {
   int nbt;
 };
 
-// The attention of one workgroup (split p, KV head kvh, selecting row s).
+// The attention of one workgroup (split p, KV head kvh, selecting row s,
+// query rows q0 .. q0 + qpw - 1 of the row's qps).
 // kFusedSel: the selection is not read from a.topk; select_fn(b, load_q)
 // computes it, calls load_q() once its own first loads are in flight, and
 // returns where the selection is.
@@ -143,7 +145,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, SelectFn&& sele
   __shared__ int32_t blk_tok[kRound];         // first token of each staged block
   __shared__ int32_t blk_pos[kRound];         // its position in the page pool (page*page_size + slot)
 
-  const int p = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  const int p = blockIdx.x, kvh = (int)blockIdx.y / a.qg, s = blockIdx.z;
+  const int q0 = ((int)blockIdx.y - kvh * a.qg) * a.qpw;
   const int l = lane_id(), w = threadIdx.x / 64;
   const int lc = l & 15, lg = l >> 4;
 
@@ -171,8 +174,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, SelectFn&& sele
       const int n = nt * 16 + lc;
       const bool real = n < a.nh;
       const int nn = real ? n : 0;
-      const int i = nn / a.G;
-      const int h = kvh * a.G + (nn - i * a.G);
+      const int i0 = nn / a.G;
+      const int i = q0 + i0;
+      const int h = kvh * a.G + (nn - i0 * a.G);
       const uint16_t* qrow = a.q + ((size_t)(s * a.qps + i) * a.Hq + h) * D;
       const int rl = a.row_seq_len[s * a.qps + i];
       rlen[nt] = real ? rl : -1;
@@ -432,7 +436,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, SelectFn&& sele
     }
     fac_lds[n][kWaves] = (Ls > 0.f) ? 1.f / Ls : 0.f;
     if (n < a.nh) {
-      const int r = s * a.qps + n / a.G;
+      const int r = s * a.qps + q0 + n / a.G;
       const int h = kvh * a.G + n % a.G;
       a.lse_part[((size_t)p * a.R + r) * a.Hq + h] = (Ls > 0.f) ? (M + log2f(Ls)) * kLn2 : -INFINITY;
     }
@@ -443,7 +447,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, SelectFn&& sele
     float v = 0.f;
 #pragma unroll
     for (int x = 0; x < kWaves; ++x) v += o_w[x][n][d] * fac_lds[n][x];
-    const int r = s * a.qps + n / a.G;
+    const int r = s * a.qps + q0 + n / a.G;
     const int h = kvh * a.G + n % a.G;
     a.o_part[(((size_t)p * a.R + r) * a.Hq + h) * D + d] = v * fac_lds[n][kWaves];
   }
@@ -482,6 +486,10 @@ constexpr bool select_decode_ok() {
   return decode_wide_ok<NH>() &&
          decode_lds_bytes<D, NH>(8) + kSelectLdsBytes + (kFusedMaxTopk + kBtLds) * 4 + 1024 <= 160 * 1024;
 }
+// the most heads one fused workgroup takes, by head dim
+constexpr int kFusedHeads128 = 8, kFusedHeads64 = 16;
+static_assert(select_decode_ok<128, kFusedHeads128>() && !select_decode_ok<128, 2 * kFusedHeads128>() &&
+              select_decode_ok<64, kFusedHeads64>(), "fused head limits");
 
 template <int D, int NH, bool FP8>
 __global__ __launch_bounds__(kFinThreads) void select_decode_kernel(DecodeArgs a, WsPtrs ws, int32_t max_seq_len,
@@ -635,6 +643,8 @@ DecodeArgs decode_args(const qsa_config& c, int32_t S, int32_t q_per_sel, int32_
   a.Hkv = c.num_kv_heads;
   a.G = c.num_q_heads / c.num_kv_heads;
   a.qps = q_per_sel;
+  a.qg = 1;
+  a.qpw = q_per_sel;
   a.nh = a.G * q_per_sel;
   a.P = P;
   a.R = S * q_per_sel;
@@ -694,14 +704,26 @@ qsa_status launch_select_decode(const qsa_config& c, int32_t S, int32_t q_per_se
                                 hipStream_t stream) {
   if (S == 0) return QSA_OK;
   if (c.head_dim != 64 && c.head_dim != 128) return fail(QSA_ERR_UNSUPPORTED, "head_dim %d not built", c.head_dim);
-  const DecodeArgs a = decode_args(c, S, q_per_sel, P, q, row_seq_len, sel_req, sel_seq_len, topk, block_table,
-                                   k_cache, v_cache, k_scale, v_scale, o_part, lse_part);
+  DecodeArgs a = decode_args(c, S, q_per_sel, P, q, row_seq_len, sel_req, sel_seq_len, topk, block_table,
+                             k_cache, v_cache, k_scale, v_scale, o_part, lse_part);
   const WsPtrs ws = ws_ptrs(lay, ws_base);
-  dim3 grid(P, c.num_kv_heads, S);
+  // The fused kernel holds up to kFusedHeads heads per workgroup: a selecting
+  // row with more query rows than fit is spread over qg workgroups per KV
+  // head (each selects the row itself and attends its own query rows).
+  const int lim = c.head_dim == 128 ? kFusedHeads128 : kFusedHeads64;
+  for (int g = 1; g <= q_per_sel; ++g) {
+    if (q_per_sel % g == 0 && a.G * (q_per_sel / g) <= lim) {
+      a.qg = g;
+      a.qpw = q_per_sel / g;
+      a.nh = a.G * a.qpw;
+      break;
+    }
+  }
+  dim3 grid(P, c.num_kv_heads * a.qg, S);
   // One launch when the decode would run 8-wave workgroups (fewer than two
   // per CU), the rows' bitmaps fit the LDS and the shape has a fused kernel;
   // otherwise the finalize and the decode, one after the other.
-  const int64_t groups = (int64_t)P * c.num_kv_heads * S;
+  const int64_t groups = (int64_t)P * c.num_kv_heads * a.qg * S;
   bool done = false;
   if (groups < kDecodeWideMaxGroups && lay.nb_stride / 64 <= kWordsLds) {
     const bool fp8 = c.kv_dtype == QSA_KV_FP8_E4M3;

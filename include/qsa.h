@@ -281,12 +281,14 @@ qsa_status qsa_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_
  * qsa_compress_index_topk or qsa_prefill_index_topk) for the same
  * num_sel_rows, max_seq_len and sel_seq_len; topk (int32 [S, k]) is written as
  * that selection would write it.  The workspace is left clean (as after a
- * selecting call).  When the decode would run fewer than two workgroups per CU
- * (num_splits * H_kv * num_sel_rows < 512), max_seq_len <= 1,048,576 and
- * q_per_sel * H_q / H_kv <= 16 (<= 8 for head_dim 128), one kernel does both:
- * every workgroup selects its row itself, so the attention starts without a
- * launch boundary or a round trip for the selection.  Otherwise the two
- * kernels run one after the other.
+ * selecting call).  One kernel does both when a workgroup can hold the heads
+ * of some g dividing q_per_sel query rows (g * H_q / H_kv <= 16, <= 8 for
+ * head_dim 128; the largest such g is taken, so q_per_sel / g workgroups share
+ * each (split, KV head, selecting row)), the decode would run fewer than two
+ * workgroups per CU (num_splits * H_kv * (q_per_sel / g) * num_sel_rows < 512)
+ * and max_seq_len <= 1,048,576: every workgroup selects its row itself, so
+ * the attention starts without a launch boundary or a round trip for the
+ * selection.  Otherwise the two kernels run one after the other.
  *   Arguments as in the two calls: workspace from
  *   qsa_index_topk_workspace_size(cfg, num_sel_rows, max_seq_len); topk is
  *   required.
