@@ -115,6 +115,8 @@ __device__ __forceinline__ float sum_lg(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+constexpr int kBtLdsMax = 4096;  // page-table entries the fused kernel stages in LDS
+
 // Where the fused kernel's selection lives (LDS), for decode_body.
 struct SelView {
   const int32_t* sel;  // the row's k selected block ids (ascending, -1 padded)
@@ -246,7 +248,16 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, SelectFn&& sele
       }
       if (tok >= 0) {
         const int pg = tok >> a.page_log2;
-        const int pid = (kFusedSel && pg < sv.nbt) ? sv.bt[pg] : bt[pg];
+        // (two loads, not one through a selected pointer: that would be a
+        // generic load, which waits for LDS and global memory alike)
+        int pid;
+        if constexpr (kFusedSel) {
+          pid = sv.bt[min(pg, kBtLdsMax - 1)];
+          asm volatile("" : "+v"(pid));  // keeps the two loads apart
+          if (pg >= sv.nbt) pid = bt[pg];
+        } else {
+          pid = bt[pg];
+        }
         pos = (pid << a.page_log2) | (tok & (page_size - 1));
       }
       blk_tok[i] = tok;
@@ -470,7 +481,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeArgs a) {
 // one the next call's scan adds into), and workgroup (0, 0) of each row writes
 // the row's top-k.  One 8-wave workgroup per (split, KV head, row), as the
 // decode.
-constexpr int kBtLds = 4096;        // page-table entries staged in LDS
+constexpr int kBtLds = kBtLdsMax;   // page-table entries staged in LDS
 constexpr int kFusedMaxTopk = 2048;  // k <= 2048 (checked by the API)
 
 template <int D, int NH>
