@@ -55,7 +55,7 @@ class Workload:
     cache covers [0, prefix_len[b]); the step appends tokens
     [prefix_len[b], final_len[b]) through qsa_compress.  Selecting row s
     (request sel_req[s], context sel_seq_len[s]) picks the blocks that the
-    q_per_sel query rows r in [s*q_per_sel, (s+1)*q_per_sel) attend.
+    query rows r with row_sel[r] == s attend (at most q_per_sel of them).
     """
     name: str
     shape: QSAShape
@@ -71,13 +71,18 @@ class Workload:
     v_cache: torch.Tensor
     k_scale: Optional[torch.Tensor]  # fp32 [num_pages, page] (fp8 only)
     v_scale: Optional[torch.Tensor]
-    q_per_sel: int
+    q_per_sel: int                 # most query rows sharing one selecting row
     sel_req: torch.Tensor          # int32 [S]
     sel_seq_len: torch.Tensor      # int32 [S]
     q_index: torch.Tensor          # int8 [S, D]
     row_seq_len: torch.Tensor      # int32 [R]
     q: torch.Tensor                # bf16 [R, H_q, d]
+    row_sel: Optional[torch.Tensor] = None  # int32 [R]: selecting row of each query row
     extra: dict = field(default_factory=dict)
+
+    def __post_init__(self):
+        if self.row_sel is None:  # rows grouped contiguously, q_per_sel per selecting row
+            self.row_sel = torch.arange(self.num_rows, dtype=torch.int32, device=self.q.device) // self.q_per_sel
 
     @property
     def num_reqs(self) -> int:
@@ -110,7 +115,7 @@ def _quant_fp8(x: torch.Tensor):
 def make_workload(shape: QSAShape, final_len: List[int], *, step_tokens: int = 1,
                   q_per_sel: int = 1, seed: int = 0, device: str = "cpu",
                   name: str = "custom", spare_pages: int = 0,
-                  shuffle_pages: bool = True) -> Workload:
+                  shuffle_pages: bool = True, rows_per_req: Optional[List[int]] = None) -> Workload:
     """Draw a workload with the given per-request final lengths.
 
     step_tokens: tokens each request appends in the step (prefix = final - step).
@@ -118,7 +123,14 @@ def make_workload(shape: QSAShape, final_len: List[int], *, step_tokens: int = 1
                  final - step_tokens + 1 + j ... when q_per_sel == step_tokens
                  (each appended token is one query row), else every row has
                  context final_len.
+    rows_per_req: uneven draft counts instead: request b appends rows_per_req[b]
+                 tokens (its prefix is final - rows_per_req[b]), each a query row
+                 of context prefix + 1 + j, all sharing the selection of the
+                 first one (row_sel maps them); 0 rows leaves the request idle.
     """
+    if rows_per_req is not None:
+        return _make_uneven(shape, final_len, rows_per_req, seed=seed, device=device, name=name,
+                            shuffle_pages=shuffle_pages)
     g = _gen(seed, device)
     D, hkv, d, page = shape.index_dim, shape.num_kv_heads, shape.head_dim, shape.page_size
     fl = np.asarray(final_len, dtype=np.int64)
@@ -170,6 +182,31 @@ def make_workload(shape: QSAShape, final_len: List[int], *, step_tokens: int = 1
         sel_seq_len=torch.as_tensor(sel_len.astype(np.int32), device=device),
         q_index=q_index,
         row_seq_len=torch.as_tensor(row_len.astype(np.int32), device=device), q=q)
+
+
+def _make_uneven(shape: QSAShape, final_len: List[int], rows_per_req: List[int], *, seed: int, device: str,
+                 name: str, shuffle_pages: bool) -> Workload:
+    n = np.asarray(rows_per_req, dtype=np.int64)
+    base = make_workload(shape, final_len, step_tokens=int(max(n.max(), 1)), q_per_sel=1, seed=seed, device=device,
+                         name=name, shuffle_pages=shuffle_pages)
+    fl = base.final_len
+    prefix = np.maximum(fl - n, 0)
+    active = np.nonzero(n > 0)[0]
+    S = active.shape[0]
+    row_len = np.concatenate([prefix[b] + 1 + np.arange(n[b]) for b in active]).astype(np.int64)
+    row_sel = np.repeat(np.arange(S), n[active])
+    g = _gen(seed + 104729, device)
+    q_index = torch.randint(-127, 128, (S, shape.index_dim), generator=g, device=device, dtype=torch.int8)
+    q = torch.randn((row_len.shape[0], shape.num_q_heads, shape.head_dim), generator=g,
+                    device=device).to(torch.bfloat16)
+    return Workload(
+        name=name, shape=shape, seed=seed, device=device, final_len=fl, prefix_len=prefix,
+        keys=base.keys, key_off=base.key_off, block_table=base.block_table, num_pages=base.num_pages,
+        k_cache=base.k_cache, v_cache=base.v_cache, k_scale=base.k_scale, v_scale=base.v_scale,
+        q_per_sel=int(n.max()), sel_req=torch.as_tensor(active.astype(np.int32), device=device),
+        sel_seq_len=torch.as_tensor((prefix[active] + 1).astype(np.int32), device=device), q_index=q_index,
+        row_seq_len=torch.as_tensor(row_len.astype(np.int32), device=device), q=q,
+        row_sel=torch.as_tensor(row_sel.astype(np.int32), device=device))
 
 
 def make_prefill_workload(shape: QSAShape, final_len: List[int], chunk, *, seed: int = 0,

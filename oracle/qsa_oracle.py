@@ -43,9 +43,11 @@ listed with its reason in the design notes of the repository):
   R9  GQA heads are grouped contiguously: query head h reads KV head h // G;
   R10 scores are scaled by softmax_scale; LSE is the natural log of the sum of
       exp(scaled logit);
-  R11 a decode split ("partition") p of P owns the contiguous run of selected
-      blocks [floor(p*n/P), floor((p+1)*n/P)) of the ascending selection, and the
-      last split also owns the tail; an empty split yields (0, -inf);
+  R11 a decode split ("partition") p of P owns a slice of the selecting row's
+      context, as a context-parallel rank owns a slice of the main KV cache: the
+      selected blocks j with floor(p*nb/P) <= j < floor((p+1)*nb/P), where
+      nb = floor(L_sel/4) is the number of closed blocks; the last split also
+      owns the tail; an empty split yields (0, -inf);
   R12 FP8 K/V is OCP E4M3 (bias 7, no infinities, S.1111.111 = NaN) times one
       fp32 scale per token per tensor.
 """
@@ -178,20 +180,30 @@ def token_positions(blocks: np.ndarray, sel_seq_len: int, row_seq_len: int) -> n
     return np.concatenate([np.sort(toks), tail])
 
 
+def split_slices(sel_seq_len: int, num_splits: int) -> List[Tuple[int, int]]:
+    """Block range [lo, hi) of each split's slice of the context (R11).
+
+    [QSA-DCP], decode context parallelism: every rank reads its own slice of
+    the main KV cache and yields a partial result.  Split p owns the closed
+    blocks floor(p*nb/P) <= j < floor((p+1)*nb/P) of the selecting row.
+    """
+    nb = sel_seq_len // COMPRESS_RATIO
+    return [((p * nb) // num_splits, ((p + 1) * nb) // num_splits) for p in range(num_splits)]
+
+
 def split_token_positions(blocks: np.ndarray, sel_seq_len: int, row_seq_len: int,
                           num_splits: int) -> List[np.ndarray]:
-    """Partition of a row's tokens into num_splits contiguous runs (R11).
-
-    The one-GPU stand-in for decode context parallelism in [QSA-DCP]: each
-    partition is read separately and the partial results are merged later.
+    """Partition of a row's tokens by context slice (R11): part p holds the
+    tokens of the selected blocks inside split p's slice, ascending, and the
+    last part also holds the row's tail (R5, R8).  Each part is attended
+    separately and the partial results are merged later, as in [QSA-DCP].
     """
     b = np.asarray(blocks, dtype=np.int64)
     b = np.sort(b[b >= 0])
-    n = b.shape[0]
     parts = []
-    for p in range(num_splits):
-        lo, hi = (p * n) // num_splits, ((p + 1) * n) // num_splits
-        toks = (b[lo:hi, None] * COMPRESS_RATIO + np.arange(COMPRESS_RATIO)[None, :]).reshape(-1)
+    for p, (lo, hi) in enumerate(split_slices(sel_seq_len, num_splits)):
+        mine = b[(b >= lo) & (b < hi)]
+        toks = (mine[:, None] * COMPRESS_RATIO + np.arange(COMPRESS_RATIO)[None, :]).reshape(-1)
         if p == num_splits - 1:
             toks = np.concatenate([toks, np.arange(tail_start(sel_seq_len), row_seq_len, dtype=np.int64)])
         parts.append(toks)
@@ -288,16 +300,18 @@ def decode_kv(raw: np.ndarray, kv_dtype: str, scales: np.ndarray = None) -> np.n
 # One decode step for a batch of rows
 # ---------------------------------------------------------------------------
 
-def decode_rows(*, q: np.ndarray, q_per_sel: int, sel_req: np.ndarray, sel_seq_len: np.ndarray,
+def decode_rows(*, q: np.ndarray, row_sel: np.ndarray, sel_req: np.ndarray, sel_seq_len: np.ndarray,
                 row_seq_len: np.ndarray, topk: np.ndarray, block_table: np.ndarray, page_size: int,
                 k_cache: np.ndarray, v_cache: np.ndarray, kv_dtype: str, scale: float,
                 num_splits: int, k_scale: np.ndarray = None, v_scale: np.ndarray = None,
                 rows: Sequence[int] = None):
     """Sparse attention for query rows, with num_splits partials and their merge.
 
-    q: bf16 bits [R, H_q, d]; row r reuses the selection of selecting row
-    s = r // q_per_sel (the MTP reuse of [PR53896] "关键源码片段"), of request
-    sel_req[s].  topk: [S, k] ascending block ids (-1 padded).
+    q: bf16 bits [R, H_q, d].  Row r uses the selection of selecting row
+    s = row_sel[r] (several rows may share one: the MTP reuse of [PR53896]
+    "关键源码片段", where later draft tokens keep the first token's top-k), of
+    request sel_req[s]; a row with row_sel[r] < 0 attends nothing and gets the
+    empty result (0, -inf).  topk: [S, k] ascending block ids (-1 padded).
     Returns dict with o_part [P, R', H_q, d], lse_part [P, R', H_q],
     out [R', H_q, d], lse [R', H_q] for the requested rows R'.
     """
@@ -308,7 +322,9 @@ def decode_rows(*, q: np.ndarray, q_per_sel: int, sel_req: np.ndarray, sel_seq_l
     o_part = np.zeros((P, len(rows), hq, d))
     lse_part = np.full((P, len(rows), hq), -np.inf)
     for i, r in enumerate(rows):
-        s = r // q_per_sel
+        s = int(row_sel[r])
+        if s < 0:
+            continue
         b = int(sel_req[s])
         qr = bf16_bits_to_f64(q[r])
         parts = split_token_positions(topk[s], int(sel_seq_len[s]), int(row_seq_len[r]), P)

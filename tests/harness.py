@@ -37,6 +37,7 @@ class HostCopy:
     sel_req: np.ndarray
     sel_seq_len: np.ndarray
     row_seq_len: np.ndarray
+    row_sel: np.ndarray
 
 
 def _bits(t: torch.Tensor) -> np.ndarray:
@@ -52,7 +53,8 @@ def host_copy(wl) -> HostCopy:
         k_scale=None if wl.k_scale is None else wl.k_scale.cpu().numpy(),
         v_scale=None if wl.v_scale is None else wl.v_scale.cpu().numpy(),
         q=_bits(wl.q), q_index=wl.q_index.cpu().numpy(), sel_req=wl.sel_req.cpu().numpy(),
-        sel_seq_len=wl.sel_seq_len.cpu().numpy(), row_seq_len=wl.row_seq_len.cpu().numpy())
+        sel_seq_len=wl.sel_seq_len.cpu().numpy(), row_seq_len=wl.row_seq_len.cpu().numpy(),
+        row_sel=wl.row_sel.cpu().numpy())
 
 
 def oracle_topk(wl, h: HostCopy, rows=None) -> np.ndarray:
@@ -68,7 +70,7 @@ def oracle_topk(wl, h: HostCopy, rows=None) -> np.ndarray:
 
 
 def oracle_decode(wl, h: HostCopy, topk: np.ndarray, num_splits: int, rows=None):
-    return O.decode_rows(q=h.q, q_per_sel=wl.q_per_sel, sel_req=h.sel_req, sel_seq_len=h.sel_seq_len,
+    return O.decode_rows(q=h.q, row_sel=h.row_sel, sel_req=h.sel_req, sel_seq_len=h.sel_seq_len,
                          row_seq_len=h.row_seq_len, topk=topk, block_table=h.block_table,
                          page_size=wl.shape.page_size, k_cache=h.k_cache, v_cache=h.v_cache,
                          kv_dtype=wl.shape.kv_dtype, scale=wl.shape.softmax_scale, num_splits=num_splits,
@@ -116,7 +118,7 @@ def ckey_blocks_from_cache(wl, ckey: np.ndarray, b: int, nb: int) -> np.ndarray:
 def check_layer(wl, layer, h=None, rows=None, topk_ref=None):
     h = h or host_copy(wl)
     tol = OUT_TOL[wl.shape.kv_dtype]
-    sel_rows = None if rows is None else sorted({r // wl.q_per_sel for r in rows})
+    sel_rows = None if rows is None else sorted({int(h.row_sel[r]) for r in rows if h.row_sel[r] >= 0})
     ref_topk = oracle_topk(wl, h, sel_rows) if topk_ref is None else topk_ref
     got_topk = layer.topk.cpu().numpy()
     srows = range(wl.num_sel) if sel_rows is None else sel_rows

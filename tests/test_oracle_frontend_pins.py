@@ -66,3 +66,52 @@ def test_norm_then_rope_differs_from_rope_then_norm_when_gains_differ():
     z = np.zeros(8)
     assert np.allclose(F.rope(F.rmsnorm(x, z), np.array([11]), 10000.0),
                        F.rmsnorm(F.rope(x, np.array([11]), 10000.0), z))   # with unit gains it does not
+
+
+def _composed_case(pos, base=10000.0):
+    """A unit hidden vector e_3 whose q projection is e_0 and k projection 2 e_1
+    (column 3 of the weight), non-uniform gains, distinct q and k scales."""
+    rng = np.random.default_rng(4)
+    H, D = 16, 8
+    w = rng.standard_normal((2 * D, H))
+    w[:, 3] = 0.0
+    w[0, 3] = 1.0            # q row 0
+    w[D + 1, 3] = 2.0        # k row 1
+    h = np.zeros((1, H))
+    h[0, 3] = 1.0
+    g_q = np.linspace(-0.5, 0.75, D)
+    g_q[0], g_q[D // 2] = 0.5, -0.25
+    g_k = np.linspace(0.3, -0.6, D)
+    g_k[1], g_k[1 + D // 2] = -0.4, 0.6
+    res = F.indexer_frontend(h, np.array([pos]), w, g_q, g_k, base, 20.0, 7.0, D, prequant=True)
+    return res, g_q, g_k, D, base
+
+
+def test_composed_front_end_at_position_zero():
+    """Position 0: no rotation; q = e_0 normalised (rms sqrt(1/D)) times (1 + g_q[0])
+    times q_scale, k = 2 e_1 normalised (rms 2 sqrt(1/D)) times (1 + g_k[1]) times k_scale."""
+    (qi, ki, qf, kf), g_q, g_k, D, _ = _composed_case(0)
+    want_q = np.zeros(D)
+    want_q[0] = 20.0 * (1 + g_q[0]) / np.sqrt(1.0 / D + F.RMS_EPS)
+    want_k = np.zeros(D)
+    want_k[1] = 7.0 * 2.0 * (1 + g_k[1]) / np.sqrt(4.0 / D + F.RMS_EPS)
+    assert np.allclose(qf[0], want_q, atol=1e-12) and np.allclose(kf[0], want_k, atol=1e-12)
+    assert qi[0].tolist() == np.rint(want_q).astype(int).tolist()
+    assert ki[0].tolist() == np.rint(want_k).astype(int).tolist()
+
+
+def test_composed_front_end_at_position_p():
+    """Position p: the normalised q's pair (0, D/2) turns by p radians and k's pair
+    (1, 1 + D/2) by p * base^(-2/D), after the gains (norm first, then rotation)."""
+    p = 3
+    (qi, ki, qf, kf), g_q, g_k, D, base = _composed_case(p)
+    vq = 20.0 * (1 + g_q[0]) / np.sqrt(1.0 / D + F.RMS_EPS)
+    vk = 7.0 * 2.0 * (1 + g_k[1]) / np.sqrt(4.0 / D + F.RMS_EPS)
+    a = p * base ** (-2.0 / D)
+    want_q = np.zeros(D)
+    want_q[0], want_q[D // 2] = vq * np.cos(p), vq * np.sin(p)
+    want_k = np.zeros(D)
+    want_k[1], want_k[1 + D // 2] = vk * np.cos(a), vk * np.sin(a)
+    assert np.allclose(qf[0], want_q, atol=1e-12) and np.allclose(kf[0], want_k, atol=1e-12)
+    assert qi[0].tolist() == np.clip(np.rint(want_q), -127, 127).astype(int).tolist()
+    assert ki[0].tolist() == np.clip(np.rint(want_k), -127, 127).astype(int).tolist()

@@ -111,3 +111,106 @@ def test_fp8_wrong_bias_is_caught(monkeypatch):
     monkeypatch.setattr(O, "fp8_e4m3_to_f64", bad)
     assert _fails(P.test_fp8_anchor_values)
     assert _fails(P.test_fp8_decode_matches_torch_all_codes)
+
+
+def test_gather_ignoring_the_block_table_is_caught(monkeypatch):
+    def bad_rows(cache, block_table_row, page_size, tokens):
+        t = np.asarray(tokens, dtype=np.int64)
+        return cache[t // page_size, :, t % page_size, :]        # identity table
+    def bad_scales(scale, block_table_row, page_size, tokens):
+        t = np.asarray(tokens, dtype=np.int64)
+        return np.asarray(scale, dtype=np.float64)[t // page_size, t % page_size]
+    monkeypatch.setattr(O, "paged_rows", bad_rows)
+    monkeypatch.setattr(O, "paged_scales", bad_scales)
+    assert _fails(P.test_paged_rows_follow_a_shuffled_block_table)
+    assert _fails(P.test_paged_scales_follow_a_shuffled_block_table)
+
+
+def test_fp8_scale_divided_instead_of_multiplied_is_caught(monkeypatch):
+    orig = O.decode_kv
+    def bad(raw, kv_dtype, scales=None):
+        if kv_dtype == "fp8":
+            return O.fp8_e4m3_to_f64(raw) / np.asarray(scales, dtype=np.float64)[:, None, None]
+        return orig(raw, kv_dtype, scales)
+    monkeypatch.setattr(O, "decode_kv", bad)
+    assert _fails(P.test_decode_kv_fp8_applies_the_token_scale)
+    assert _fails(P.test_decode_kv_fp8_inverts_per_token_quantisation)
+
+
+def test_front_end_rotation_before_norm_is_caught(monkeypatch):
+    import oracle.qsa_frontend_oracle as F
+    import tests.test_oracle_frontend_pins as FP
+    def bad(hidden, positions, w_qk, g_q, g_k, base, q_scale, k_scale, D, prequant=False):
+        q, k = F.project(hidden, w_qk, D)
+        q = F.rmsnorm(F.rope(q, positions, base), g_q)
+        k = F.rmsnorm(F.rope(k, positions, base), g_k)
+        if prequant:
+            return F.quantize(q, q_scale), F.quantize(k, k_scale), q * q_scale, k * k_scale
+        return F.quantize(q, q_scale), F.quantize(k, k_scale)
+    monkeypatch.setattr(F, "indexer_frontend", bad)
+    assert _fails(FP.test_composed_front_end_at_position_p)
+
+
+def test_front_end_swapped_scales_is_caught(monkeypatch):
+    import oracle.qsa_frontend_oracle as F
+    import tests.test_oracle_frontend_pins as FP
+    orig = F.indexer_frontend
+    def bad(hidden, positions, w_qk, g_q, g_k, base, q_scale, k_scale, D, prequant=False):
+        return orig(hidden, positions, w_qk, g_q, g_k, base, k_scale, q_scale, D, prequant)
+    monkeypatch.setattr(F, "indexer_frontend", bad)
+    assert _fails(FP.test_composed_front_end_at_position_zero)
+    assert _fails(FP.test_composed_front_end_at_position_p)
+
+
+def test_front_end_swapped_gains_is_caught(monkeypatch):
+    import oracle.qsa_frontend_oracle as F
+    import tests.test_oracle_frontend_pins as FP
+    orig = F.indexer_frontend
+    def bad(hidden, positions, w_qk, g_q, g_k, base, q_scale, k_scale, D, prequant=False):
+        return orig(hidden, positions, w_qk, g_k, g_q, base, q_scale, k_scale, D, prequant)
+    monkeypatch.setattr(F, "indexer_frontend", bad)
+    assert _fails(FP.test_composed_front_end_at_position_zero)
+
+
+def test_split_by_position_in_the_selection_is_caught(monkeypatch):
+    """The split rule of runs of the ascending selection (not slices of the context)."""
+    def bad(blocks, sel_seq_len, row_seq_len, num_splits):
+        b = np.asarray(blocks, dtype=np.int64)
+        b = np.sort(b[b >= 0])
+        n, parts = b.shape[0], []
+        for p in range(num_splits):
+            lo, hi = (p * n) // num_splits, ((p + 1) * n) // num_splits
+            toks = (b[lo:hi, None] * 4 + np.arange(4)[None, :]).reshape(-1)
+            if p == num_splits - 1:
+                toks = np.concatenate([toks, np.arange(O.tail_start(sel_seq_len), row_seq_len)])
+            parts.append(toks)
+        return parts
+    monkeypatch.setattr(O, "split_token_positions", bad)
+    assert _fails(P.test_split_worked_example_slices_of_the_context)
+    assert _fails(P.test_split_parts_stay_inside_their_context_slices, 700)
+
+
+def test_rows_ignoring_row_sel_is_caught(monkeypatch):
+    orig = O.decode_rows
+    def bad(**kw):
+        rs = np.asarray(kw["row_sel"])
+        kw["row_sel"] = np.where(rs >= 0, np.minimum(np.arange(rs.shape[0]), len(kw["sel_req"]) - 1), -1)
+        return orig(**kw)
+    monkeypatch.setattr(O, "decode_rows", bad)
+    assert _fails(P.test_rows_follow_row_sel_with_their_own_tails, "bf16")
+
+
+def test_rows_ignoring_sel_req_is_caught(monkeypatch):
+    orig = O.decode_rows
+    def bad(**kw):
+        kw["sel_req"] = np.arange(len(kw["sel_req"]))
+        return orig(**kw)
+    monkeypatch.setattr(O, "decode_rows", bad)
+    assert _fails(P.test_rows_follow_row_sel_with_their_own_tails, "fp8")
+
+
+def test_tail_of_the_selecting_row_instead_of_the_own_row_is_caught(monkeypatch):
+    orig = O.split_token_positions
+    monkeypatch.setattr(O, "split_token_positions",
+                        lambda blocks, sel_seq_len, row_seq_len, P_: orig(blocks, sel_seq_len, sel_seq_len, P_))
+    assert _fails(P.test_rows_follow_row_sel_with_their_own_tails, "bf16")

@@ -137,7 +137,7 @@ def _dense_case(L, hq=4, hkv=2, d=32, seed=0, k=512):
     kc = K.permute(1, 0, 2).unsqueeze(0).contiguous().view(torch.int16).numpy()
     vc = V.permute(1, 0, 2).unsqueeze(0).contiguous().view(torch.int16).numpy()
     topk = O.index_topk_row(qi, keys, L, k)[None]
-    res = O.decode_rows(q=q.view(torch.int16).numpy(), q_per_sel=1, sel_req=np.array([0]),
+    res = O.decode_rows(q=q.view(torch.int16).numpy(), row_sel=np.array([0]), sel_req=np.array([0]),
                         sel_seq_len=np.array([L]), row_seq_len=np.array([L]), topk=topk,
                         block_table=np.array([[0]]), page_size=max(L, 1), k_cache=kc, v_cache=vc,
                         kv_dtype="bf16", scale=1 / math.sqrt(d), num_splits=1)
@@ -223,6 +223,34 @@ def test_split_partition_covers_token_set(L):
             assert p.shape[0] % 4 == 0  # block boundaries
 
 
+def test_split_worked_example_slices_of_the_context():
+    """Split p owns the selected blocks in its slice of the context: 10 closed
+    blocks (L = 42) over 3 splits are the slices [0, 3), [3, 6), [6, 10); the
+    selected blocks 1, 2, 5, 7, 9 fall as {1, 2}, {5}, {7, 9}, and the last split
+    also takes the row's tail 40, 41 (and 42, 43 for a reuse row of length 44)."""
+    blocks = np.array([1, 2, 5, 7, 9, -1, -1], dtype=np.int32)
+    parts = O.split_token_positions(blocks, 42, 44, 3)
+    assert [p.tolist() for p in parts] == [[4, 5, 6, 7, 8, 9, 10, 11], [20, 21, 22, 23],
+                                           [28, 29, 30, 31, 36, 37, 38, 39, 40, 41, 42, 43]]
+    # more splits than blocks: the empty slices yield empty parts
+    parts = O.split_token_positions(np.array([0, 1], dtype=np.int32), 9, 9, 4)
+    assert [p.tolist() for p in parts] == [[], [0, 1, 2, 3], [], [4, 5, 6, 7, 8]]
+
+
+@pytest.mark.parametrize("L", [700, 703])
+def test_split_parts_stay_inside_their_context_slices(L):
+    """Every token of part p lies in split p's slice of the context (a context-parallel
+    rank only reads its own slice of the KV cache); the tail is the context's end."""
+    topk, *_ = _row_inputs(L)
+    nb = L // 4
+    for P in [1, 2, 3, 8, 64, 100]:
+        parts = O.split_token_positions(topk, L, L, P)
+        for p, toks in enumerate(parts):
+            lo_tok = 4 * ((p * nb) // P)
+            hi_tok = 4 * (((p + 1) * nb) // P) if p < P - 1 else L
+            assert ((toks >= lo_tok) & (toks < hi_tok)).all()
+
+
 @pytest.mark.parametrize("L", [700, 703])
 def test_merge_invariant_to_partition(L):
     topk, q, K, V = _row_inputs(L)
@@ -267,3 +295,165 @@ def test_reuse_rows_attend_selection_plus_own_tail():
         t = O.token_positions(topk, sel_L, L)
         assert t.shape[0] == 64 * 4 + (L - 1000)
         assert (t[64 * 4:] == np.arange(1000, L)).all()
+
+
+# ---------------------------------------------------------------- paged storage
+
+def _scatter_to_pages(logical, table, page):
+    """Place logical rows [L, ...] into pages by explicit loops: token t goes to
+    page table[t // page], slot t % page (cache [num_pages, H, page, d] layout)."""
+    L, hkv, d = logical.shape
+    num_pages = int(np.max(table)) + 1
+    cache = np.zeros((num_pages, hkv, page, d), dtype=logical.dtype)
+    for t in range(L):
+        for g in range(hkv):
+            cache[table[t // page], g, t % page, :] = logical[t, g, :]
+    return cache
+
+
+def test_paged_rows_follow_a_shuffled_block_table():
+    """A gather through a shuffled multi-page table returns the logical rows:
+    token t sits at page table[t // page], slot t % page."""
+    r = rng(21)
+    L, hkv, d, page = 200, 2, 8, 16
+    npg = (L + page - 1) // page
+    logical = r.integers(-1000, 1000, (L, hkv, d)).astype(np.int16)
+    table = r.permutation(3 * npg)[:npg]            # scattered over a larger pool
+    cache = _scatter_to_pages(logical, table, page)
+    toks = np.array([0, 1, 15, 16, 17, 63, 64, 100, 150, 199, 5, 5])
+    got = O.paged_rows(cache, table, page, toks)
+    assert np.array_equal(got, logical[toks])
+    # the same content as one contiguous page gives the same rows
+    contig = logical.transpose(1, 0, 2)[None]       # [1, H, L, d]
+    assert np.array_equal(O.paged_rows(contig, np.array([0]), L, toks), logical[toks])
+
+
+def test_paged_scales_follow_a_shuffled_block_table():
+    r = rng(22)
+    L, page = 130, 16
+    npg = (L + page - 1) // page
+    logical = r.standard_normal(L)
+    table = r.permutation(2 * npg)[:npg]
+    scales = np.full((2 * npg, page), np.nan)
+    for t in range(L):
+        scales[table[t // page], t % page] = logical[t]
+    toks = np.arange(L)[::-1]
+    assert np.array_equal(O.paged_scales(scales, table, page, toks), logical[toks])
+
+
+# ---------------------------------------------------------------- fp8 with scales
+
+def test_decode_kv_fp8_applies_the_token_scale():
+    """Closed form: E4M3 codes 0x38 = 1, 0x40 = 2, 0xB8 = -1, 0x7E = 448 times
+    each token's own scale (scale != 1 everywhere)."""
+    raw = np.array([0x38, 0x40, 0xB8, 0x7E], dtype=np.uint8).reshape(4, 1, 1)
+    raw = np.broadcast_to(raw, (4, 2, 3)).copy()
+    scales = np.array([0.5, 3.0, 10.0, 0.25])
+    got = O.decode_kv(raw, "fp8", scales)
+    want = np.array([0.5, 6.0, -10.0, 112.0])
+    assert np.array_equal(got, np.broadcast_to(want[:, None, None], (4, 2, 3)))
+
+
+def test_decode_kv_fp8_inverts_per_token_quantisation():
+    """N(0,1) rows quantised per token (scale = amax / 448, torch's E4M3 cast,
+    an independent routine) decode back within half an E4M3 step: 2^-4 of the
+    value for normal codes, 2^-10 of the scale for subnormal ones."""
+    g = torch.Generator().manual_seed(23)
+    x = torch.randn(64, 2, 16, generator=g, dtype=torch.float64) * torch.exp(torch.randn(64, 1, 1, generator=g,
+                                                                                        dtype=torch.float64))
+    amax = x.abs().amax(dim=(1, 2))
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    codes = (x / scale[:, None, None]).to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    dec = O.decode_kv(codes, "fp8", scale.numpy())
+    xs = x.numpy()
+    bound = np.maximum(2.0 ** -4 * np.abs(xs), 2.0 ** -10 * scale.numpy()[:, None, None])
+    assert (np.abs(dec - xs) <= bound * (1 + 1e-12)).all()
+    assert np.abs(dec - xs).max() > 0                 # the test can see an error at all
+
+
+# ---------------------------------------------------------------- rows -> selecting rows
+
+def _sdpa_ref(qbits, Kl, Vl, toks, hq, hkv, scale):
+    """Dense attention of one row over the given logical tokens, by torch's
+    scaled_dot_product_attention in float64 (a library routine, not the oracle)."""
+    q = torch.from_numpy(O.bf16_bits_to_f64(qbits)).reshape(1, hq, 1, -1)
+    if len(toks) == 0:
+        return np.zeros((hq, q.shape[-1])), np.full(hq, -np.inf)
+    K = torch.from_numpy(Kl[toks]).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None]
+    V = torch.from_numpy(Vl[toks]).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None]
+    out = torch.nn.functional.scaled_dot_product_attention(q, K, V, scale=scale)[0, :, 0].numpy()
+    lse = torch.logsumexp((q @ K.transpose(-1, -2))[0, :, 0] * scale, dim=-1).numpy()
+    return out, lse
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_rows_follow_row_sel_with_their_own_tails(kv_dtype):
+    """Rows map to selecting rows unevenly (two rows share one, three share
+    another, one row is padding), selecting rows map to requests out of order,
+    and the caches are paged through shuffled tables.  Each row must equal
+    dense attention (torch) over the token set written out here: its selecting
+    row's blocks plus its own tail [4 floor(L_sel/4), L_row)."""
+    r = rng(31)
+    hq, hkv, d, D, k, page = 4, 2, 16, 8, 6, 16
+    lens = [203, 150, 97]                    # requests' cached tokens
+    sel_req = np.array([2, 0, 1])            # selecting row -> request
+    sel_len = np.array([93, 150, 141])       # within each request's tokens
+    row_sel = np.array([1, 0, 2, 1, -1, 2, 2, 0])
+    row_len = np.array([150, 95, 141, 150, 50, 143, 144, 97])
+    keys = [r.integers(-127, 128, (L, D)).astype(np.int8) for L in lens]
+    qidx = r.integers(-127, 128, (3, D)).astype(np.int8)
+    topk = np.stack([O.index_topk_row(qidx[s], keys[sel_req[s]], int(sel_len[s]), k) for s in range(3)])
+    g = torch.Generator().manual_seed(32)
+    logical_K, logical_V, kraw, vraw, ksc, vsc = [], [], [], [], [], []
+    pool = 3 * sum((L + page - 1) // page for L in lens)
+    perm = r.permutation(pool)
+    tables, off = np.zeros((3, 13), dtype=np.int64), 0
+    for b, L in enumerate(lens):
+        n = (L + page - 1) // page
+        tables[b, :n] = perm[off:off + n]
+        off += n
+    for L in lens:
+        for store, logical, scl in ((kraw, logical_K, ksc), (vraw, logical_V, vsc)):
+            x = torch.randn(L, hkv, d, generator=g, dtype=torch.float64)
+            if kv_dtype == "bf16":
+                xb = x.to(torch.bfloat16)
+                store.append(xb.view(torch.int16).numpy())
+                logical.append(xb.to(torch.float64).numpy())
+            else:
+                sc = x.abs().amax(dim=(1, 2)) / 448.0
+                c8 = (x / sc[:, None, None]).to(torch.float32).to(torch.float8_e4m3fn)
+                store.append(c8.view(torch.uint8).numpy())
+                logical.append((c8.to(torch.float64) * sc[:, None, None]).numpy())
+                scl.append(sc.numpy())
+    dt = np.int16 if kv_dtype == "bf16" else np.uint8
+    k_cache = np.zeros((pool, hkv, page, d), dtype=dt)
+    v_cache = np.zeros((pool, hkv, page, d), dtype=dt)
+    k_scale = np.zeros((pool, page))
+    v_scale = np.zeros((pool, page))
+    for b, L in enumerate(lens):
+        for t in range(L):
+            pg, sl = tables[b][t // page], t % page
+            k_cache[pg, :, sl, :] = kraw[b][t]
+            v_cache[pg, :, sl, :] = vraw[b][t]
+            if kv_dtype == "fp8":
+                k_scale[pg, sl], v_scale[pg, sl] = ksc[b][t], vsc[b][t]
+    q = torch.randn(len(row_sel), hq, d, generator=g).to(torch.bfloat16).view(torch.int16).numpy()
+    scale = 1 / math.sqrt(d)
+    res = O.decode_rows(q=q, row_sel=row_sel, sel_req=sel_req, sel_seq_len=sel_len, row_seq_len=row_len,
+                        topk=topk, block_table=tables, page_size=page, k_cache=k_cache, v_cache=v_cache,
+                        kv_dtype=kv_dtype, scale=scale, num_splits=3,
+                        k_scale=k_scale if kv_dtype == "fp8" else None,
+                        v_scale=v_scale if kv_dtype == "fp8" else None)
+    for rr, s in enumerate(row_sel):
+        if s < 0:
+            assert (res["out"][rr] == 0).all() and np.isneginf(res["lse"][rr]).all()
+            continue
+        b = sel_req[s]
+        toks = []
+        for j in topk[s]:
+            if j >= 0:
+                toks += [4 * j, 4 * j + 1, 4 * j + 2, 4 * j + 3]
+        toks += list(range(4 * (sel_len[s] // 4), row_len[rr]))
+        ref_o, ref_l = _sdpa_ref(q[rr], logical_K[b], logical_V[b], np.array(toks), hq, hkv, scale)
+        np.testing.assert_allclose(res["out"][rr], ref_o, atol=1e-12)
+        np.testing.assert_allclose(res["lse"][rr], ref_l, atol=1e-12)
