@@ -53,8 +53,9 @@ SIGNATURES = {
     "qsa_compress_index_topk": (_I, [_CFG, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P,
                                      ctypes.c_size_t, _P]),
     "qsa_prefill_index_topk": (_I, [_CFG, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
-    "qsa_sparse_decode": (_I, [_CFG, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
-    "qsa_select_sparse_decode": (_I, [_CFG, _I, _I, _I, _I] + [_P] * 13 + [ctypes.c_size_t, _P]),
+    "qsa_sparse_decode": (_I, [_CFG, _I, _I, _I, _I] + [_P] * 14),
+    "qsa_select_sparse_decode": (_I, [_CFG, _I, _I, _I, _I, _I] + [_P] * 14 + [ctypes.c_size_t, _P]),
+    "qsa_select_sparse_decode_launches": (_I, [_CFG, _I, _I, _I, _I]),
     "qsa_merge_partials": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P]),
     "qsa_indexer_project_workspace_size": (ctypes.c_size_t, [_I, _I, _I]),
     "qsa_indexer_project": (_I, [_I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_float,

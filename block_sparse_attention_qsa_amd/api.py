@@ -159,20 +159,30 @@ def qsa_prefill_index_topk(cfg: QSAConfig, q_index: torch.Tensor, row_cu: torch.
                                               workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def _row_map(q: torch.Tensor, row_sel: Optional[torch.Tensor], sel_req: torch.Tensor,
+             max_rows_per_sel: Optional[int]):
+    R, S = q.shape[0], sel_req.shape[0]
+    if row_sel is None:
+        return R, S, 1
+    _dt(row_sel, torch.int32)
+    return R, S, int(max_rows_per_sel if max_rows_per_sel is not None else R)
+
+
 def qsa_sparse_decode(cfg: QSAConfig, q: torch.Tensor, row_seq_len: torch.Tensor,
                       sel_req: torch.Tensor, sel_seq_len: torch.Tensor, topk: torch.Tensor,
                       block_table: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                      o_part: torch.Tensor, lse_part: torch.Tensor, q_per_sel: int = 1,
-                      k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
-                      stream=None) -> None:
-    """Split partials of sparse attention: o_part fp32 [P, R, H_q, d], lse_part fp32 [P, R, H_q]."""
+                      o_part: torch.Tensor, lse_part: torch.Tensor, row_sel: Optional[torch.Tensor] = None,
+                      max_rows_per_sel: Optional[int] = None, k_scale: Optional[torch.Tensor] = None,
+                      v_scale: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Split partials of sparse attention: o_part fp32 [P, R, H_q, d], lse_part fp32 [P, R, H_q].
+    Row r uses selecting row row_sel[r] (int32 [R]; None: row r is selecting row r)."""
     _dt(q, torch.bfloat16); _dt(o_part, torch.float32); _dt(lse_part, torch.float32)
     _dt(row_seq_len, torch.int32); _dt(sel_req, torch.int32); _dt(sel_seq_len, torch.int32)
     _dt(topk, torch.int32); _dt(block_table, torch.int32)
     c = cfg.to_c()
-    S = sel_req.shape[0]
+    R, S, mr = _row_map(q, row_sel, sel_req, max_rows_per_sel)
     P = o_part.shape[0]
-    _check(_lib.load().qsa_sparse_decode(ctypes.byref(c), S, int(q_per_sel), P, _ptr(q), _ptr(row_seq_len),
+    _check(_lib.load().qsa_sparse_decode(ctypes.byref(c), R, S, mr, P, _ptr(q), _ptr(row_sel), _ptr(row_seq_len),
                                          _ptr(sel_req), _ptr(sel_seq_len), _ptr(topk), _ptr(block_table),
                                          _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                                          _ptr(o_part), _ptr(lse_part), _stream(stream)))
@@ -182,7 +192,8 @@ def qsa_select_sparse_decode(cfg: QSAConfig, q: torch.Tensor, row_seq_len: torch
                              sel_req: torch.Tensor, sel_seq_len: torch.Tensor, block_table: torch.Tensor,
                              k_cache: torch.Tensor, v_cache: torch.Tensor, topk: torch.Tensor,
                              o_part: torch.Tensor, lse_part: torch.Tensor, workspace: torch.Tensor,
-                             max_seq_len: int, q_per_sel: int = 1, k_scale: Optional[torch.Tensor] = None,
+                             max_seq_len: int, row_sel: Optional[torch.Tensor] = None,
+                             max_rows_per_sel: Optional[int] = None, k_scale: Optional[torch.Tensor] = None,
                              v_scale: Optional[torch.Tensor] = None, stream=None) -> None:
     """The selection of a scored workspace (left by an index call with topk=None) into topk, then
     qsa_sparse_decode on it: o_part fp32 [P, R, H_q, d], lse_part fp32 [P, R, H_q]."""
@@ -190,13 +201,21 @@ def qsa_select_sparse_decode(cfg: QSAConfig, q: torch.Tensor, row_seq_len: torch
     _dt(row_seq_len, torch.int32); _dt(sel_req, torch.int32); _dt(sel_seq_len, torch.int32)
     _dt(topk, torch.int32); _dt(block_table, torch.int32)
     c = cfg.to_c()
-    S = sel_req.shape[0]
+    R, S, mr = _row_map(q, row_sel, sel_req, max_rows_per_sel)
     P = o_part.shape[0]
     _check(_lib.load().qsa_select_sparse_decode(
-        ctypes.byref(c), S, int(q_per_sel), P, int(max_seq_len), _ptr(q), _ptr(row_seq_len), _ptr(sel_req),
+        ctypes.byref(c), R, S, mr, P, int(max_seq_len), _ptr(q), _ptr(row_sel), _ptr(row_seq_len), _ptr(sel_req),
         _ptr(sel_seq_len), _ptr(block_table), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(topk), _ptr(o_part), _ptr(lse_part), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def qsa_select_sparse_decode_launches(cfg: QSAConfig, num_sel_rows: int, max_rows_per_sel: int, num_splits: int,
+                                      max_seq_len: int) -> int:
+    """Kernel launches qsa_select_sparse_decode makes for this shape (1: fused, 2: finalize + attention)."""
+    c = cfg.to_c()
+    return int(_lib.load().qsa_select_sparse_decode_launches(ctypes.byref(c), num_sel_rows, max_rows_per_sel,
+                                                             num_splits, max_seq_len))
 
 
 def qsa_merge_partials(o_part: torch.Tensor, lse_part: torch.Tensor, out: torch.Tensor,

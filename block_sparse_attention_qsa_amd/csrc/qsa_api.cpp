@@ -222,24 +222,29 @@ qsa_status qsa_prefill_index_topk(const qsa_config* cfg, int32_t num_reqs, int32
 
 // Argument checks of the attention half (qsa_sparse_decode and the fused call);
 // `what` names the call in the messages.
-static qsa_status check_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_t q_per_sel, int32_t num_splits,
-                               const void* q, const int32_t* row_seq_len, const int32_t* sel_req,
-                               const int32_t* sel_seq_len, const int32_t* topk, const int32_t* block_table,
-                               const void* k_cache, const void* v_cache, const float* k_scale,
-                               const float* v_scale, const float* o_part, const float* lse_part,
-                               const char* what) {
+static qsa_status check_decode(const qsa_config* cfg, int32_t num_rows, int32_t num_sel_rows,
+                               int32_t max_rows_per_sel, int32_t num_splits, const void* q, const int32_t* row_sel,
+                               const int32_t* row_seq_len, const int32_t* sel_req, const int32_t* sel_seq_len,
+                               const int32_t* topk, const int32_t* block_table, const void* k_cache,
+                               const void* v_cache, const float* k_scale, const float* v_scale,
+                               const float* o_part, const float* lse_part, const char* what) {
   if (num_sel_rows < 0 || num_sel_rows > 65535)
     return fail(QSA_ERR_INVALID_ARGUMENT, "num_sel_rows must be in [0, 65535] (got %d)", num_sel_rows);
+  if (num_rows < 0 || num_rows > (1 << 24))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "num_rows must be in [0, 2^24] (got %d)", num_rows);
   if (num_splits < 1 || num_splits > 64)
     return fail(QSA_ERR_INVALID_ARGUMENT, "num_splits must be in [1, 64] (got %d)", num_splits);
-  if (q_per_sel < 1) return fail(QSA_ERR_INVALID_ARGUMENT, "q_per_sel must be >= 1 (got %d)", q_per_sel);
+  if (max_rows_per_sel < 1)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "max_rows_per_sel must be >= 1 (got %d)", max_rows_per_sel);
   const int G = cfg->num_q_heads / cfg->num_kv_heads;
-  if ((int64_t)G * q_per_sel > 64)
-    return fail(QSA_ERR_UNSUPPORTED, "q_per_sel * (num_q_heads/num_kv_heads) = %lld exceeds 64",
-                (long long)G * q_per_sel);
-  if ((int64_t)num_sel_rows * q_per_sel > (1 << 24))
-    return fail(QSA_ERR_INVALID_ARGUMENT, "too many query rows");
-  if (num_sel_rows == 0) return QSA_OK;
+  if ((int64_t)G * max_rows_per_sel > 64)
+    return fail(QSA_ERR_UNSUPPORTED, "max_rows_per_sel * (num_q_heads/num_kv_heads) = %lld exceeds 64",
+                (long long)G * max_rows_per_sel);
+  if (!row_sel && (num_rows != num_sel_rows || max_rows_per_sel != 1))
+    return fail(QSA_ERR_INVALID_ARGUMENT,
+                "%s: without row_sel every row is its own selecting row (num_rows == num_sel_rows, "
+                "max_rows_per_sel == 1)", what);
+  if (num_sel_rows == 0 || num_rows == 0) return QSA_OK;
   if (!q || !row_seq_len || !sel_req || !sel_seq_len || !topk || !block_table || !k_cache || !v_cache ||
       !o_part || !lse_part)
     return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL array argument", what);
@@ -254,8 +259,9 @@ static qsa_status check_decode(const qsa_config* cfg, int32_t num_sel_rows, int3
 
 extern "C" {
 
-qsa_status qsa_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_t q_per_sel,
-                             int32_t num_splits, const void* q, const int32_t* row_seq_len,
+qsa_status qsa_sparse_decode(const qsa_config* cfg, int32_t num_rows, int32_t num_sel_rows,
+                             int32_t max_rows_per_sel, int32_t num_splits, const void* q,
+                             const int32_t* row_sel, const int32_t* row_seq_len,
                              const int32_t* sel_req, const int32_t* sel_seq_len,
                              const int32_t* topk, const int32_t* block_table,
                              const void* k_cache, const void* v_cache,
@@ -263,19 +269,20 @@ qsa_status qsa_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_
                              float* o_part, float* lse_part, hipStream_t stream) {
   qsa_status st = check_config(cfg, false, true);
   if (st != QSA_OK) return st;
-  st = check_decode(cfg, num_sel_rows, q_per_sel, num_splits, q, row_seq_len, sel_req, sel_seq_len, topk,
-                    block_table, k_cache, v_cache, k_scale, v_scale, o_part, lse_part, "qsa_sparse_decode");
-  if (st != QSA_OK || num_sel_rows == 0) return st;
-  return launch_sparse_decode(*cfg, num_sel_rows, q_per_sel, num_splits, q, row_seq_len, sel_req,
-                              sel_seq_len, topk, block_table, k_cache, v_cache, k_scale, v_scale,
+  st = check_decode(cfg, num_rows, num_sel_rows, max_rows_per_sel, num_splits, q, row_sel, row_seq_len, sel_req,
+                    sel_seq_len, topk, block_table, k_cache, v_cache, k_scale, v_scale, o_part, lse_part,
+                    "qsa_sparse_decode");
+  if (st != QSA_OK || num_sel_rows == 0 || num_rows == 0) return st;
+  return launch_sparse_decode(*cfg, num_rows, num_sel_rows, max_rows_per_sel, num_splits, q, row_sel, row_seq_len,
+                              sel_req, sel_seq_len, topk, block_table, k_cache, v_cache, k_scale, v_scale,
                               o_part, lse_part, stream);
 }
 
-qsa_status qsa_select_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_t q_per_sel,
-                                    int32_t num_splits, int32_t max_seq_len, const void* q,
-                                    const int32_t* row_seq_len, const int32_t* sel_req,
-                                    const int32_t* sel_seq_len, const int32_t* block_table,
-                                    const void* k_cache, const void* v_cache,
+qsa_status qsa_select_sparse_decode(const qsa_config* cfg, int32_t num_rows, int32_t num_sel_rows,
+                                    int32_t max_rows_per_sel, int32_t num_splits, int32_t max_seq_len,
+                                    const void* q, const int32_t* row_sel, const int32_t* row_seq_len,
+                                    const int32_t* sel_req, const int32_t* sel_seq_len,
+                                    const int32_t* block_table, const void* k_cache, const void* v_cache,
                                     const float* k_scale, const float* v_scale, int32_t* topk,
                                     float* o_part, float* lse_part,
                                     void* workspace, size_t ws_bytes, hipStream_t stream) {
@@ -283,18 +290,31 @@ qsa_status qsa_select_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows,
   if (st != QSA_OK) return st;
   if (max_seq_len < 0 || max_seq_len > QSA_MAX_SEQ_LEN)
     return fail(QSA_ERR_INVALID_ARGUMENT, "max_seq_len must be in [0, %d] (got %d)", QSA_MAX_SEQ_LEN, max_seq_len);
-  st = check_decode(cfg, num_sel_rows, q_per_sel, num_splits, q, row_seq_len, sel_req, sel_seq_len, topk,
-                    block_table, k_cache, v_cache, k_scale, v_scale, o_part, lse_part, "qsa_select_sparse_decode");
+  st = check_decode(cfg, num_rows, num_sel_rows, max_rows_per_sel, num_splits, q, row_sel, row_seq_len, sel_req,
+                    sel_seq_len, topk, block_table, k_cache, v_cache, k_scale, v_scale, o_part, lse_part,
+                    "qsa_select_sparse_decode");
   if (st != QSA_OK || num_sel_rows == 0) return st;
+  if (num_rows == 0 && !topk) return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_select_sparse_decode: topk is NULL");
   TopkWorkspace lay = topk_workspace_layout(num_sel_rows, max_seq_len);
   if (!workspace) return fail(QSA_ERR_WORKSPACE, "qsa_select_sparse_decode: workspace is NULL");
   if (!aligned(workspace, 256)) return fail(QSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (ws_bytes < lay.total)
     return fail(QSA_ERR_WORKSPACE, "qsa_select_sparse_decode: workspace has %zu bytes, needs %zu", ws_bytes,
                 lay.total);
-  return launch_select_decode(*cfg, num_sel_rows, q_per_sel, num_splits, max_seq_len, q, row_seq_len, sel_req,
-                              sel_seq_len, block_table, k_cache, v_cache, k_scale, v_scale, topk, o_part,
-                              lse_part, lay, workspace, stream);
+  return launch_select_decode(*cfg, num_rows, num_sel_rows, max_rows_per_sel, num_splits, max_seq_len, q, row_sel,
+                              row_seq_len, sel_req, sel_seq_len, block_table, k_cache, v_cache, k_scale, v_scale,
+                              topk, o_part, lse_part, lay, workspace, stream);
+}
+
+int32_t qsa_select_sparse_decode_launches(const qsa_config* cfg, int32_t num_sel_rows, int32_t max_rows_per_sel,
+                                          int32_t num_splits, int32_t max_seq_len) {
+  if (check_config(cfg, true, true) != QSA_OK) return 0;
+  if (num_sel_rows < 1 || num_sel_rows > 65535 || max_rows_per_sel < 1 || num_splits < 1 || num_splits > 64 ||
+      max_seq_len < 0 || max_seq_len > QSA_MAX_SEQ_LEN)
+    return 0;
+  const int G = cfg->num_q_heads / cfg->num_kv_heads;
+  if ((int64_t)G * max_rows_per_sel > 64) return 0;
+  return select_decode_launches(*cfg, num_sel_rows, max_rows_per_sel, num_splits, max_seq_len);
 }
 
 qsa_status qsa_merge_partials(int32_t num_splits, int32_t num_rows, int32_t num_heads,

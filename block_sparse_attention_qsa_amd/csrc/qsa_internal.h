@@ -70,20 +70,23 @@ qsa_status launch_indexer_project(int32_t T, int32_t H, int32_t D, const void* h
                                   const void* w_qk, const float* g_q, const float* g_k, float base, float q_scale,
                                   float k_scale, int8_t* q_index, int8_t* keys, float* ws, hipStream_t stream);
 
-qsa_status launch_sparse_decode(const qsa_config& c, int32_t S, int32_t q_per_sel, int32_t P,
-                                const void* q, const int32_t* row_seq_len, const int32_t* sel_req,
-                                const int32_t* sel_seq_len, const int32_t* topk,
+qsa_status launch_sparse_decode(const qsa_config& c, int32_t R, int32_t S, int32_t qps, int32_t P,
+                                const void* q, const int32_t* row_sel, const int32_t* row_seq_len,
+                                const int32_t* sel_req, const int32_t* sel_seq_len, const int32_t* topk,
                                 const int32_t* block_table, const void* k_cache,
                                 const void* v_cache, const float* k_scale, const float* v_scale,
                                 float* o_part, float* lse_part, hipStream_t stream);
 
 // Selection (finalize of a scored workspace) fused with qsa_sparse_decode.
-qsa_status launch_select_decode(const qsa_config& c, int32_t S, int32_t q_per_sel, int32_t P, int32_t max_seq_len,
-                                const void* q, const int32_t* row_seq_len, const int32_t* sel_req,
-                                const int32_t* sel_seq_len, const int32_t* block_table, const void* k_cache,
-                                const void* v_cache, const float* k_scale, const float* v_scale, int32_t* topk,
-                                float* o_part, float* lse_part, const TopkWorkspace& lay, void* ws_base,
-                                hipStream_t stream);
+qsa_status launch_select_decode(const qsa_config& c, int32_t R, int32_t S, int32_t qps, int32_t P,
+                                int32_t max_seq_len, const void* q, const int32_t* row_sel,
+                                const int32_t* row_seq_len, const int32_t* sel_req, const int32_t* sel_seq_len,
+                                const int32_t* block_table, const void* k_cache, const void* v_cache,
+                                const float* k_scale, const float* v_scale, int32_t* topk, float* o_part,
+                                float* lse_part, const TopkWorkspace& lay, void* ws_base, hipStream_t stream);
+
+// Kernel launches qsa_select_sparse_decode makes for this shape: 1 (fused) or 2.
+int select_decode_launches(const qsa_config& c, int32_t S, int32_t qps, int32_t P, int32_t max_seq_len);
 
 // The finalize kernel alone (qsa_index_topk's selection step).
 qsa_status launch_finalize_ws(const qsa_config& c, int32_t rows, const int32_t* seq_len, int32_t max_seq_len,

@@ -450,6 +450,299 @@ __device__ __forceinline__ void select_row(int s, const int32_t* __restrict__ se
   }
 }
 
+// ---------------------------------------------------------------------------
+// Selection for one split of a row (the fused selection + attention kernel).
+//
+// Split p of P owns the run [floor(p ks / P), floor((p+1) ks / P)) of the row's
+// ks ascending selected blocks (a contiguous stretch of the context with a
+// near-equal share of the selection).  Every workgroup serving the row finds
+// the selection itself, as select_row does: the threshold bin T from the
+// histogram, the chunks' lists classified against it (blocks above T marked in
+// an LDS bitmap of the row, bin-T blocks listed as candidates), and the radix
+// select of the bin-T winners, marked too.  emit_run() then lists only the
+// workgroup's own run, ascending: a popcount prefix sum over the bitmap, with
+// the bit walk confined to the words that hold the run.
+struct RowLds {
+  uint32_t sh[kFinThreads / 64];
+  __align__(16) uint32_t rhist[kRadixPasses][256];
+  uint64_t cand[kCandLds];
+  uint64_t bm[kWordsLds];  // the row's selection (rows of up to kWordsLds * 64 blocks)
+  int32_t T;
+  uint32_t above, n, nfb;
+  uint16_t fb[kMaxChunksPerRow];  // chunks read again from their scores
+};
+
+struct RowSelector {
+  RowLds& L;
+  int s;
+  int32_t k;
+  WsPtrs ws;
+  // set by first()
+  int nb = 0, nwords = 0, nchunks = 0, T = 0, tpc = 1, cpr = 1, sub = 0;
+  uint32_t ks = 0, above = 0;
+
+  __device__ __forceinline__ void mark(uint32_t j) {
+    atomicOr(reinterpret_cast<unsigned long long*>(&L.bm[j >> 6]), 1ull << (j & 63));
+  }
+
+  // The loads, the threshold bin and the classification.  hook(): once the
+  // first round of loads is in flight; mid(): by all threads right before the
+  // barrier that ends the classification.
+  template <class Hook, class Mid>
+  __device__ __forceinline__ void first(const int32_t* __restrict__ sel_seq_len, int32_t max_seq_len, uint32_t t,
+                                        Hook&& hook, Mid&& mid) {
+    constexpr int kPer = kBins / kFinThreads;
+    static_assert(kPer == 4 && kFinKeys == 8, "vector loads of the first round");
+    const int tid = threadIdx.x;
+    const int nchunks_max = ws.nb_stride / kScoreChunk;
+    tpc = chunk_threads(ws.nb_stride);
+    cpr = kFinThreads / tpc;
+    sub = tid % tpc;
+    const uint32_t* ghist0 = ws.hist + (size_t)s * kBins;
+    const uint32_t* cinfo = ws.cinfo + (size_t)s * nchunks_max;
+    const uint64_t* ckeys = ws.keys + (size_t)s * ws.nb_stride;
+    const int32_t* srow = ws.scores + (size_t)s * ws.nb_stride;
+
+    // First round, one 16-byte load per four histogram bins or two keys: both
+    // histogram rows (bins 2047 - 4 tid - i, i < 4: descending), the chunk's
+    // cinfo and the first kFinKeys keys of its list.
+    const uint4 hv0 = *reinterpret_cast<const uint4*>(ghist0 + kBins - 4 - 4 * tid);
+    const uint4 hv1 = *reinterpret_cast<const uint4*>(ghist0 + ws.hist_stride + kBins - 4 - 4 * tid);
+    int cc = min(tid / tpc, nchunks_max - 1);
+    uint32_t ci = cinfo[cc];
+    uint64_t kk[kFinKeys];
+    auto load_keys = [&](int c) {
+      const i32x4* kp = reinterpret_cast<const i32x4*>(ckeys + (size_t)c * kScoreChunk + sub * kFinKeys);
+#pragma unroll
+      for (int e = 0; e < kFinKeys / 2; ++e) {
+        const i32x4 v = kp[e];
+        kk[2 * e] = (uint64_t)(uint32_t)v[0] | ((uint64_t)(uint32_t)v[1] << 32);
+        kk[2 * e + 1] = (uint64_t)(uint32_t)v[2] | ((uint64_t)(uint32_t)v[3] << 32);
+      }
+    };
+    load_keys(cc);
+    const int Lr = sel_seq_len[s];
+    hook();
+    asm volatile("" ::"s"(Lr));
+    uint32_t hc[kPer];
+    {
+      asm volatile("" ::"v"(hv0.x), "v"(hv0.y), "v"(hv0.z), "v"(hv0.w), "v"(hv1.x), "v"(hv1.y), "v"(hv1.z),
+                   "v"(hv1.w));
+      const uint4 h = (t & 1u) ? hv1 : hv0;
+      hc[0] = h.w; hc[1] = h.z; hc[2] = h.y; hc[3] = h.x;
+    }
+    const int Lc = min(Lr, max_seq_len);
+    nb = max(Lc, 0) >> 2;
+    if (nb == 0) {  // nothing was scored: no blocks, the histogram is untouched
+      mid();
+      __syncthreads();
+      return;
+    }
+    ks = (uint32_t)min(k, nb);
+    nwords = (nb + 63) >> 6;  // <= kWordsLds (checked by the host)
+    nchunks = (nb + kScoreChunk - 1) / kScoreChunk;
+    for (int i = tid; i < nwords; i += kFinThreads) L.bm[i] = 0;
+    for (int i = tid; i < kRadixPasses * 64; i += kFinThreads)
+      reinterpret_cast<uint4*>(&L.rhist[0][0])[i] = uint4{0u, 0u, 0u, 0u};
+    if (tid == 0) { L.n = 0; L.T = 0; L.above = 0; L.nfb = 0; }
+    threshold_from_counts<kFinThreads>(hc, ks, L.sh, &L.T, &L.above);
+    asm volatile("" ::"v"(ci));
+#pragma unroll
+    for (int e = 0; e < kFinKeys; ++e) asm volatile("" ::"v"(kk[e]));
+    T = L.T;
+    above = L.above;
+
+    auto classify = [&](uint64_t key) {
+      const int bin = score_bin(key_score(key));
+      if (bin > T) {
+        mark(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+      } else if (bin == T) {
+        const uint32_t i = atomicAdd(&L.n, 1u);
+        if (i < (uint32_t)kCandLds) L.cand[i] = key;
+      }
+    };
+    for (int c0 = 0; c0 < nchunks; c0 += cpr) {
+      const int c = c0 + tid / tpc;
+      if (c0 > 0) {
+        cc = min(c, nchunks_max - 1);
+        ci = cinfo[cc];
+        load_keys(cc);
+      }
+      uint32_t at_t = 0;
+      if (c < nchunks) {
+        const uint32_t cnt = ci >> 16;
+        const int lb = (int)(ci & 0xffffu);
+        if (lb <= T) {  // the list holds every block of this chunk with bin >= T
+#pragma unroll
+          for (int e = 0; e < kFinKeys; ++e) {
+            const int bin = score_bin(key_score(kk[e]));
+            const bool valid = (uint32_t)(sub * kFinKeys + e) < cnt;
+            if (valid && bin > T) mark(0xffffffffu - (uint32_t)(kk[e] & 0xffffffffull));
+            at_t |= (valid && bin == T) ? 1u << e : 0u;
+          }
+          for (uint32_t i = (uint32_t)(tpc * kFinKeys + sub); i < cnt; i += tpc)
+            classify(ckeys[(size_t)c * kScoreChunk + i]);
+        } else if (sub == 0) {  // local bin above T: bins [T, lb) are not listed
+          L.fb[atomicAdd(&L.nfb, 1u)] = (uint16_t)c;
+        }
+      }
+      const uint32_t na = (uint32_t)__builtin_popcount(at_t);
+      const uint32_t incl = wave_incl_scan(na);
+      const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      if (wtot) {
+        uint32_t base = 0;
+        if (lane_id() == 0) base = atomicAdd(&L.n, wtot);
+        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+        uint32_t pos = base + incl - na;
+#pragma unroll
+        for (int e = 0; e < kFinKeys; ++e) {
+          if ((at_t & (1u << e)) && pos < (uint32_t)kCandLds) L.cand[pos] = kk[e];
+          pos += (at_t >> e) & 1u;
+        }
+      }
+    }
+    mid();
+    __syncthreads();
+    constexpr int kFbChunks = 4;
+    constexpr int kFbIters = kScoreChunk / kFinThreads;
+    const uint32_t nfb = L.nfb;
+    for (uint32_t f0 = 0; f0 < nfb; f0 += kFbChunks) {
+      int32_t fs[kFbChunks][kFbIters];
+      int fc[kFbChunks];
+#pragma unroll
+      for (int q = 0; q < kFbChunks; ++q) {
+        fc[q] = L.fb[min(f0 + q, nfb - 1)];
+#pragma unroll
+        for (int it = 0; it < kFbIters; ++it) fs[q][it] = srow[fc[q] * kScoreChunk + it * kFinThreads + tid];
+      }
+#pragma unroll
+      for (int q = 0; q < kFbChunks; ++q) {
+#pragma unroll
+        for (int it = 0; it < kFbIters; ++it) {
+          const int j = fc[q] * kScoreChunk + it * kFinThreads + tid;
+          if (f0 + q < nfb && j < nb) classify(cand_key(fs[q][it], (uint32_t)j));
+        }
+      }
+    }
+    if (nfb) __syncthreads();
+  }
+
+  // The radix select of the bin-T winners (as in select_row), marked in the
+  // bitmap; ends with a barrier.
+  __device__ __forceinline__ void second() {
+    const int tid = threadIdx.x;
+    if (nb == 0) return;
+    const int nchunks_max = ws.nb_stride / kScoreChunk;
+    const uint32_t* cinfo = ws.cinfo + (size_t)s * nchunks_max;
+    const uint64_t* ckeys = ws.keys + (size_t)s * ws.nb_stride;
+    const int32_t* srow = ws.scores + (size_t)s * ws.nb_stride;
+    const uint32_t n = L.n;
+    const uint32_t need = ks - above;  // 1 <= need <= n
+    constexpr uint64_t kBinMask = ~((1ull << (32 + kBinShift)) - 1ull);
+    if (n <= (uint32_t)kCandLds) {
+      const uint64_t mine = L.cand[min((uint32_t)tid, n - 1)];
+      uint64_t prefix = 0, mask = 0;
+      if (need < n) {
+        mask = kBinMask;
+        prefix = L.cand[0] & kBinMask;
+        uint32_t rem = need;
+        for (int pass = 0, shift = 32 + kBinShift - 8;; ++pass, shift = max(shift - 8, 0)) {
+          uint32_t* h = L.rhist[pass];
+          if ((uint32_t)tid < n && (mine & mask) == prefix) atomicAdd(&h[(mine >> shift) & 0xff], 1u);
+          for (uint32_t i = tid + kFinThreads; i < n; i += kFinThreads) {
+            const uint64_t key = L.cand[i];
+            if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 0xff], 1u);
+          }
+          __syncthreads();
+          uint32_t dsel, larger, cnt;
+          radix_digit(h, rem, dsel, larger, cnt);
+          rem -= larger;
+          prefix = (prefix & ~(0xffull << shift)) | ((uint64_t)dsel << shift);
+          mask |= 0xffull << shift;
+          if (cnt == rem || shift == 0) break;
+        }
+      }
+      if ((uint32_t)tid < n && (mine & mask) >= prefix) mark(0xffffffffu - (uint32_t)(mine & 0xffffffffull));
+      for (uint32_t i = tid + kFinThreads; i < n; i += kFinThreads) {
+        const uint64_t key = L.cand[i];
+        if ((key & mask) >= prefix) mark(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+      }
+    } else {
+      // More bin-T candidates than the LDS holds (massive ties): every pass
+      // and the marking visit them where the classification found them.
+      auto visit = [&](auto&& f) {
+        for (int c0 = 0; c0 < nchunks; c0 += cpr) {
+          const int c = c0 + tid / tpc;
+          if (c >= nchunks) continue;
+          const uint32_t cinf = cinfo[c];
+          if ((int)(cinf & 0xffffu) <= T) {
+            const uint32_t cnt = cinf >> 16;
+            for (uint32_t i = sub; i < cnt; i += tpc) {
+              const uint64_t key = ckeys[(size_t)c * kScoreChunk + i];
+              if (score_bin(key_score(key)) == T) f(key);
+            }
+          } else {
+            const int jn = min(kScoreChunk, nb - c * kScoreChunk);
+            for (int i = sub; i < jn; i += tpc) {
+              const uint32_t j = (uint32_t)(c * kScoreChunk + i);
+              const uint64_t key = cand_key(srow[j], j);
+              if (score_bin(key_score(key)) == T) f(key);
+            }
+          }
+        }
+      };
+      uint64_t mask = kBinMask, prefix = L.cand[0] & kBinMask;
+      uint32_t rem = need;
+      for (int pass = 0, shift = 32 + kBinShift - 8;; ++pass, shift = max(shift - 8, 0)) {
+        uint32_t* h = L.rhist[pass];
+        visit([&](uint64_t key) {
+          if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 0xff], 1u);
+        });
+        __syncthreads();
+        uint32_t dsel, larger, cnt;
+        radix_digit(h, rem, dsel, larger, cnt);
+        rem -= larger;
+        prefix = (prefix & ~(0xffull << shift)) | ((uint64_t)dsel << shift);
+        mask |= 0xffull << shift;
+        if (cnt == rem || shift == 0) break;
+      }
+      visit([&](uint64_t key) {
+        if ((key & mask) >= prefix) mark(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+      });
+    }
+    __syncthreads();
+  }
+
+  // The selected blocks at positions [i0, i1) of the row's ascending selection
+  // into list[0, i1 - i0) (LDS); each(i, j) is called for list entry i = block
+  // j.  Block-wide: ends with a barrier.
+  template <class Each>
+  __device__ __forceinline__ void emit_run(int i0, int i1, int32_t* list, Each&& each) {
+    if (nb == 0) return;
+    const int tid = threadIdx.x;
+    const int per = (nwords + kFinThreads - 1) / kFinThreads;
+    const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
+    uint32_t cntw = 0;
+    for (int i = w0; i < w1; ++i) cntw += (uint32_t)__popcll(L.bm[i]);
+    uint32_t pos = block_excl_scan<kFinThreads, false>(cntw, L.sh);
+    if ((int)pos < i1 && (int)(pos + cntw) > i0) {  // this thread's words hold part of the run
+      for (int i = w0; i < w1; ++i) {
+        uint64_t m = L.bm[i];
+        while (m) {
+          const int bit = __ffsll((long long)m) - 1;
+          m &= m - 1;
+          if ((int)pos >= i0 && (int)pos < i1) {
+            list[pos - i0] = i * 64 + bit;
+            each((int)pos - i0, i * 64 + bit);
+          }
+          ++pos;
+        }
+      }
+    }
+    __syncthreads();
+  }
+};
+
 // After the selection of the call counted t: row s of the other histogram,
 // the one the next scan adds into, back to zero (the workgroup's threads share
 // it; the last call that used it finished before this call's scan began).

@@ -77,6 +77,10 @@ class QSALayer:
         self.step_max_new = int((wl.final_len - wl.prefix_len).max()) if B else 0
         self.fused = bool(fuse_append) and self.step_max_new <= 5
         self.select_decode = bool(select_decode)
+        # one row per selecting row, in order: no row map (the library's identity)
+        ident = wl.num_rows == wl.num_sel and wl.q_per_sel == 1 and bool(
+            (wl.row_sel.cpu() == torch.arange(wl.num_rows, dtype=torch.int32)).all())
+        self.row_sel = None if ident else wl.row_sel
 
     def prefill(self, chunk: Optional[int] = None) -> None:
         """Bulk-compress every request's prefix [0, prefix_len) (optionally in chunks)."""
@@ -114,15 +118,17 @@ class QSALayer:
         wl = self.wl
         api.qsa_sparse_decode(self.cfg, wl.q, wl.row_seq_len, wl.sel_req, wl.sel_seq_len, self.topk,
                               wl.block_table, wl.k_cache, wl.v_cache, self.o_part, self.lse_part,
-                              q_per_sel=wl.q_per_sel, k_scale=wl.k_scale, v_scale=wl.v_scale, stream=stream)
+                              row_sel=self.row_sel, max_rows_per_sel=wl.q_per_sel, k_scale=wl.k_scale,
+                              v_scale=wl.v_scale, stream=stream)
 
     def select_attend(self, stream=None) -> None:
         """Selection of the scored workspace into topk, then the attention (one call)."""
         wl = self.wl
         api.qsa_select_sparse_decode(self.cfg, wl.q, wl.row_seq_len, wl.sel_req, wl.sel_seq_len, wl.block_table,
                                      wl.k_cache, wl.v_cache, self.topk, self.o_part, self.lse_part,
-                                     self.workspace, self.max_seq_len, q_per_sel=wl.q_per_sel,
-                                     k_scale=wl.k_scale, v_scale=wl.v_scale, stream=stream)
+                                     self.workspace, self.max_seq_len, row_sel=self.row_sel,
+                                     max_rows_per_sel=wl.q_per_sel, k_scale=wl.k_scale, v_scale=wl.v_scale,
+                                     stream=stream)
 
     def merge(self, stream=None) -> None:
         api.qsa_merge_partials(self.o_part, self.lse_part, self.out, self.lse, stream=stream)

@@ -241,29 +241,38 @@ qsa_status qsa_prefill_index_topk(const qsa_config* cfg, int32_t num_reqs, int32
 /*
  * qsa_sparse_decode -- attention of the query rows over the selected tokens,
  * as num_splits partial results.  [QSA-DCP]: softmax and value aggregation over
- * the uncompressed K/V at the kept positions; each context-parallel partition
- * yields a partial result that is merged at the end (qsa_merge_partials).
+ * the uncompressed K/V at the kept positions; with decode context parallelism
+ * each rank reads its own slice of the main KV cache and yields a partial
+ * result, merged at the end (qsa_merge_partials).
  *
- * Rows r = s*q_per_sel + i (i < q_per_sel) share selecting row s: same request
- * sel_req[s], same topk[s] ([PR53896]: a later MTP step reuses the selection).
- * Row r attends tokens {4j..4j+3 : j in topk[s], j >= 0} plus its own tail
- * [4*floor(sel_seq_len[s]/4), row_seq_len[r]) (the open block it could not
- * score).  row_seq_len[r] >= sel_seq_len[s] is required.
- * Split p of P owns selected blocks [floor(p*n/P), floor((p+1)*n/P)) of the n
- * valid ones, and split P-1 also owns the tail.  For query head h (KV head
- * h / (H_q/H_kv)):
+ * Query row r (0 <= r < num_rows) uses selecting row s = row_sel[r]: request
+ * sel_req[s], selection topk[s] ([PR53896]: a later MTP step reuses the first
+ * step's selection; any number of draft rows per request, in any order).  It
+ * attends tokens {4j..4j+3 : j in topk[s], j >= 0} plus its own tail
+ * [4*floor(sel_seq_len[s]/4), row_seq_len[r]) (the open block the selecting
+ * row could not score); row_seq_len[r] >= sel_seq_len[s] is required.
+ *   row_sel  int32 [num_rows], or NULL: row r is selecting row r (then
+ *            num_rows == num_sel_rows and max_rows_per_sel == 1).  Rows with
+ *            row_sel[r] outside [0, num_sel_rows), and rows past the first
+ *            max_rows_per_sel (in index order) of one selecting row, are not
+ *            attended: their o_part / lse_part entries are not written.
+ * Split p of P owns a slice of the selecting row's context: the selected
+ * blocks j with floor(p*nb/P) <= j < floor((p+1)*nb/P), nb = floor(sel_seq_len/4);
+ * split P-1 also owns the tail.  For query head h (KV head h / (H_q/H_kv)):
  *   z_t = softmax_scale * q[r][h] . K_t   (fp8: times k_scale of token t)
  *   lse_part[p][r][h] = log sum_t exp(z_t)                 (natural log)
  *   o_part[p][r][h][:] = sum_t exp(z_t - lse) V_t          (fp8: V_t * v_scale_t)
- * An empty split gives o_part = 0, lse_part = -inf.
- *   q        bf16 [S*q_per_sel, H_q, d]
- *   o_part   fp32 [P, S*q_per_sel, H_q, d];  lse_part fp32 [P, S*q_per_sel, H_q]
- *   num_splits in [1, 64]; q_per_sel * (H_q/H_kv) <= 64.
+ * A split without tokens gives o_part = 0, lse_part = -inf.
+ *   q        bf16 [num_rows, H_q, d]
+ *   topk     int32 [num_sel_rows, k]: ascending block ids, then -1 (as qsa_index_topk writes)
+ *   o_part   fp32 [P, num_rows, H_q, d];  lse_part fp32 [P, num_rows, H_q]
+ *   num_splits in [1, 64]; max_rows_per_sel * (H_q/H_kv) <= 64.
  *   k_scale / v_scale are required for fp8 and ignored for bf16.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (head_dim, group size), HIP.
  */
-qsa_status qsa_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_t q_per_sel,
-                             int32_t num_splits, const void* q, const int32_t* row_seq_len,
+qsa_status qsa_sparse_decode(const qsa_config* cfg, int32_t num_rows, int32_t num_sel_rows,
+                             int32_t max_rows_per_sel, int32_t num_splits, const void* q,
+                             const int32_t* row_sel, const int32_t* row_seq_len,
                              const int32_t* sel_req, const int32_t* sel_seq_len,
                              const int32_t* topk, const int32_t* block_table,
                              const void* k_cache, const void* v_cache,
@@ -276,33 +285,40 @@ qsa_status qsa_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_
  * blocks, then softmax and value aggregation over the kept positions, as
  * context-parallel partials).  Its outputs are exactly those of
  *   qsa_index_topk(..., topk, workspace, ...)   (the selection half), then
- *   qsa_sparse_decode(cfg, num_sel_rows, q_per_sel, num_splits, ..., topk, ...)
+ *   qsa_sparse_decode(cfg, num_rows, num_sel_rows, max_rows_per_sel, num_splits, ...)
  * on a workspace left by a scoring call with topk == NULL (qsa_index_topk,
  * qsa_compress_index_topk or qsa_prefill_index_topk) for the same
  * num_sel_rows, max_seq_len and sel_seq_len; topk (int32 [S, k]) is written as
- * that selection would write it.  The workspace is left clean (as after a
- * selecting call).  One kernel does both when a workgroup can hold the heads
- * of some g dividing q_per_sel query rows (g * H_q / H_kv <= 16, <= 8 for
- * head_dim 128; the largest such g is taken, so q_per_sel / g workgroups share
- * each (split, KV head, selecting row)), the decode would run fewer than two
- * workgroups per CU (num_splits * H_kv * (q_per_sel / g) * num_sel_rows < 512)
- * and max_seq_len <= 1,048,576: every workgroup selects its row itself, so
- * the attention starts without a launch boundary or a round trip for the
- * selection.  Otherwise the two kernels run one after the other.
+ * that selection would write it, and the partials are the same, bit for bit.
+ * The workspace is left clean (as after a selecting call).  One kernel does
+ * both (qsa_select_sparse_decode_launches returns 1) when the grid of
+ * P x H_kv x row groups x S workgroups has fewer than 512 (row groups: the
+ * fewest groups of query rows whose heads fit one workgroup, 8 heads at
+ * head_dim 128 and 16 at 64) and a row's selection bitmap fits the LDS
+ * (max_seq_len up to about 1,048,576 tokens): each workgroup finds its row's
+ * selection itself and lists only its own run, so the attention starts
+ * without a launch boundary.  Otherwise the two kernels run one after the
+ * other.
  *   Arguments as in the two calls: workspace from
  *   qsa_index_topk_workspace_size(cfg, num_sel_rows, max_seq_len); topk is
- *   required.
+ *   required; num_rows = 0 only selects.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (index_dim, head_dim, group size),
  *         WORKSPACE, HIP.
  */
-qsa_status qsa_select_sparse_decode(const qsa_config* cfg, int32_t num_sel_rows, int32_t q_per_sel,
-                                    int32_t num_splits, int32_t max_seq_len, const void* q,
-                                    const int32_t* row_seq_len, const int32_t* sel_req,
-                                    const int32_t* sel_seq_len, const int32_t* block_table,
-                                    const void* k_cache, const void* v_cache,
+qsa_status qsa_select_sparse_decode(const qsa_config* cfg, int32_t num_rows, int32_t num_sel_rows,
+                                    int32_t max_rows_per_sel, int32_t num_splits, int32_t max_seq_len,
+                                    const void* q, const int32_t* row_sel, const int32_t* row_seq_len,
+                                    const int32_t* sel_req, const int32_t* sel_seq_len,
+                                    const int32_t* block_table, const void* k_cache, const void* v_cache,
                                     const float* k_scale, const float* v_scale, int32_t* topk,
                                     float* o_part, float* lse_part,
                                     void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Kernel launches qsa_select_sparse_decode makes for this shape: 1 (selection
+ * and attention in one kernel) or 2 (finalize, then attention); 0 on a bad
+ * argument.  Enqueues nothing. */
+int32_t qsa_select_sparse_decode_launches(const qsa_config* cfg, int32_t num_sel_rows, int32_t max_rows_per_sel,
+                                          int32_t num_splits, int32_t max_seq_len);
 
 /*
  * qsa_merge_partials -- log-sum-exp merge of the split partials ([QSA-DCP]:

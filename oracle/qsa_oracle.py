@@ -43,11 +43,12 @@ listed with its reason in the design notes of the repository):
   R9  GQA heads are grouped contiguously: query head h reads KV head h // G;
   R10 scores are scaled by softmax_scale; LSE is the natural log of the sum of
       exp(scaled logit);
-  R11 a decode split ("partition") p of P owns a slice of the selecting row's
-      context, as a context-parallel rank owns a slice of the main KV cache: the
-      selected blocks j with floor(p*nb/P) <= j < floor((p+1)*nb/P), where
-      nb = floor(L_sel/4) is the number of closed blocks; the last split also
-      owns the tail; an empty split yields (0, -inf);
+  R11 a decode split ("partition") p of P owns a contiguous slice of the
+      context, as a context-parallel rank does; the slice boundaries are the
+      selection's quantiles, so that the splits hold near-equal shares: split p
+      owns the selected blocks [floor(p*n/P), floor((p+1)*n/P)) of the n
+      ascending selected blocks, and the last split also owns the tail; an
+      empty split yields (0, -inf);
   R12 FP8 K/V is OCP E4M3 (bias 7, no infinities, S.1111.111 = NaN) times one
       fp32 scale per token per tensor.
 """
@@ -180,30 +181,23 @@ def token_positions(blocks: np.ndarray, sel_seq_len: int, row_seq_len: int) -> n
     return np.concatenate([np.sort(toks), tail])
 
 
-def split_slices(sel_seq_len: int, num_splits: int) -> List[Tuple[int, int]]:
-    """Block range [lo, hi) of each split's slice of the context (R11).
-
-    [QSA-DCP], decode context parallelism: every rank reads its own slice of
-    the main KV cache and yields a partial result.  Split p owns the closed
-    blocks floor(p*nb/P) <= j < floor((p+1)*nb/P) of the selecting row.
-    """
-    nb = sel_seq_len // COMPRESS_RATIO
-    return [((p * nb) // num_splits, ((p + 1) * nb) // num_splits) for p in range(num_splits)]
-
-
 def split_token_positions(blocks: np.ndarray, sel_seq_len: int, row_seq_len: int,
                           num_splits: int) -> List[np.ndarray]:
-    """Partition of a row's tokens by context slice (R11): part p holds the
-    tokens of the selected blocks inside split p's slice, ascending, and the
-    last part also holds the row's tail (R5, R8).  Each part is attended
-    separately and the partial results are merged later, as in [QSA-DCP].
+    """Partition of a row's tokens into num_splits contiguous runs (R11).
+
+    The one-GPU stand-in for decode context parallelism in [QSA-DCP]: each
+    partition covers a contiguous stretch of the context, is attended
+    separately, and the partial results are merged later.  Part p holds the
+    selected blocks [floor(p*n/P), floor((p+1)*n/P)) of the n ascending ones;
+    the last part also holds the row's tail (R5, R8).
     """
     b = np.asarray(blocks, dtype=np.int64)
     b = np.sort(b[b >= 0])
+    n = b.shape[0]
     parts = []
-    for p, (lo, hi) in enumerate(split_slices(sel_seq_len, num_splits)):
-        mine = b[(b >= lo) & (b < hi)]
-        toks = (mine[:, None] * COMPRESS_RATIO + np.arange(COMPRESS_RATIO)[None, :]).reshape(-1)
+    for p in range(num_splits):
+        lo, hi = (p * n) // num_splits, ((p + 1) * n) // num_splits
+        toks = (b[lo:hi, None] * COMPRESS_RATIO + np.arange(COMPRESS_RATIO)[None, :]).reshape(-1)
         if p == num_splits - 1:
             toks = np.concatenate([toks, np.arange(tail_start(sel_seq_len), row_seq_len, dtype=np.int64)])
         parts.append(toks)

@@ -122,10 +122,11 @@ def test_prefill_index_topk_rejects(lib):
     assert pf(B=0) == 0
 
 
-def decode(lib, c, P=2, qps=1, S=4, **kw):
+def decode(lib, c, P=2, mr=1, S=4, R=None, rs=FAKE, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, o=FAKE, l=FAKE)
     a.update(kw)
-    return lib.qsa_sparse_decode(ctypes.byref(c), S, qps, P, a["q"], FAKE, FAKE, FAKE, FAKE, FAKE,
+    R = S if R is None else R
+    return lib.qsa_sparse_decode(ctypes.byref(c), R, S, mr, P, a["q"], rs, FAKE, FAKE, FAKE, FAKE, FAKE,
                                  a["k"], a["v"], a["ks"], a["vs"], a["o"], a["l"], None)
 
 
@@ -136,34 +137,56 @@ def test_decode_rejects(lib):
     assert decode(lib, cfg(softmax_scale=0.0)) == 1
     assert decode(lib, cfg(), P=0) == 1
     assert decode(lib, cfg(), P=65) == 1
-    assert decode(lib, cfg(), qps=0) == 1
-    assert decode(lib, cfg(), qps=9) == 2          # 8 heads x 9 rows > 64
+    assert decode(lib, cfg(), mr=0) == 1
+    assert decode(lib, cfg(), mr=9) == 2          # 8 heads x 9 rows > 64
+    assert decode(lib, cfg(), R=-1) == 1
+    assert decode(lib, cfg(), rs=None, R=5) == 1  # no row map: one row per selecting row
+    assert decode(lib, cfg(), rs=None, mr=2) == 1
     assert decode(lib, cfg(kv_dtype=1)) == 1       # fp8 without scales
     assert decode(lib, cfg(), q=None) == 1
     assert decode(lib, cfg(), k=ctypes.c_void_p(0x10008)) == 1
     assert decode(lib, cfg(), S=0) == 0
+    assert decode(lib, cfg(), R=0) == 0
 
 
 def test_select_sparse_decode_rejects(lib):
     c = cfg()
     n = lib.qsa_index_topk_workspace_size(ctypes.byref(c), 4, 65536)
 
-    def sd(c=c, S=4, qps=1, P=2, L=65536, ws=FAKE, nbytes=n, topk=FAKE, q=FAKE, ks=None, vs=None):
-        return lib.qsa_select_sparse_decode(ctypes.byref(c), S, qps, P, L, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                            ks, vs, topk, FAKE, FAKE, ws, nbytes, None)
+    def sd(c=c, S=4, R=4, mr=1, P=2, L=65536, ws=FAKE, nbytes=n, topk=FAKE, q=FAKE, ks=None, vs=None, rs=FAKE):
+        return lib.qsa_select_sparse_decode(ctypes.byref(c), R, S, mr, P, L, q, rs, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            FAKE, ks, vs, topk, FAKE, FAKE, ws, nbytes, None)
     assert sd(c=cfg(index_dim=96)) == 2             # the selection's config check
     assert sd(c=cfg(head_dim=96)) == 2              # the attention's
     assert sd(c=cfg(num_q_heads=15)) == 1
     assert sd(L=_lib.QSA_MAX_SEQ_LEN + 4) == 1
     assert sd(P=0) == 1
-    assert sd(qps=9) == 2
+    assert sd(mr=9) == 2
     assert sd(topk=None) == 1                       # the selection is an output here
+    assert sd(topk=None, R=0) == 1
     assert sd(q=None) == 1
     assert sd(c=cfg(kv_dtype=1)) == 1               # fp8 without scales
     assert sd(nbytes=n - 1) == 3
     assert sd(ws=None) == 3
     assert sd(ws=ctypes.c_void_p(0x10010)) == 3
     assert sd(S=0) == 0
+
+
+def test_select_sparse_decode_reports_its_launches(lib):
+    """One kernel while the grid stays under two workgroups per CU, the rows'
+    selection bitmaps fit the LDS and a row's heads fit a workgroup (8 at
+    head_dim 128, 16 at 64); else the finalize and the attention."""
+    c = cfg()   # 16 query heads over 2 KV heads: 8 heads per row
+    f = lambda S, mr, P, L, c=c: lib.qsa_select_sparse_decode_launches(ctypes.byref(c), S, mr, P, L)
+    assert f(8, 1, 16, 262144) == 1                 # 16 x 2 x 8 = 256 workgroups
+    assert f(8, 1, 32, 262144) == 2                 # 512 workgroups
+    assert f(128, 1, 1, 262144) == 1                # the mixed batch: 256
+    assert f(4, 4, 8, 1000003) == 1                 # 4 rows x 8 heads: 4 row groups, 256 workgroups
+    assert f(4, 4, 16, 1000003) == 2                # 512 workgroups
+    assert f(4, 1, 2, 1200000) == 2                 # rows past 262,144 blocks: the bitmap is in the workspace
+    assert f(4, 1, 2, 100, cfg(num_q_heads=16, num_kv_heads=1)) == 2   # 16 heads of one row at d = 128
+    assert f(4, 1, 2, 100, cfg(num_q_heads=16, num_kv_heads=1, head_dim=64)) == 1
+    assert f(0, 1, 2, 100) == 0 and f(4, 9, 2, 100) == 0
 
 
 def test_merge_rejects(lib):

@@ -48,10 +48,10 @@ def _attend_and_check(layer, wl, h, sel_len, row_len, topk, what):
     sel_t = torch.as_tensor(np.asarray(sel_len, np.int32), device=DEV)
     row_t = torch.as_tensor(np.asarray(row_len, np.int32), device=DEV)
     api.qsa_sparse_decode(layer.cfg, wl.q, row_t, wl.sel_req, sel_t, torch.as_tensor(topk, device=DEV),
-                          wl.block_table, wl.k_cache, wl.v_cache, layer.o_part, layer.lse_part, q_per_sel=1)
+                          wl.block_table, wl.k_cache, wl.v_cache, layer.o_part, layer.lse_part)
     api.qsa_merge_partials(layer.o_part, layer.lse_part, layer.out, layer.lse)
     torch.cuda.synchronize()
-    ref = O.decode_rows(q=h.q, q_per_sel=1, sel_req=h.sel_req, sel_seq_len=np.asarray(sel_len),
+    ref = O.decode_rows(q=h.q, row_sel=np.arange(wl.num_rows), sel_req=h.sel_req, sel_seq_len=np.asarray(sel_len),
                         row_seq_len=np.asarray(row_len), topk=topk, block_table=h.block_table,
                         page_size=wl.shape.page_size, k_cache=h.k_cache, v_cache=h.v_cache,
                         kv_dtype=wl.shape.kv_dtype, scale=wl.shape.softmax_scale, num_splits=layer.P,

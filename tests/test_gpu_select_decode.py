@@ -5,17 +5,20 @@ Its contract is the selection half of qsa_index_topk followed by
 qsa_sparse_decode.  Every case checks the selection bit for bit and the
 partials / outputs within the bars against the oracle, and compares with the
 two separate calls on the same inputs: the selection and the partials must
-be identical (same kernels' arithmetic), bit for bit.  Shapes cover the one-
+be identical (same kernels' arithmetic, same order), bit for bit.  Shapes cover the one-
 launch kernel (few workgroups, head groups up to 16, d = 64 and 128, bf16 and
-fp8, selecting rows whose query rows are spread over several workgroups) and
-the two-launch fallback (large grids, 16 heads per KV head at d = 128), rows
-with fewer than k blocks, rows with nothing scored, and rows whose threshold
-bin holds more candidates than the LDS (massive ties).
+fp8, selecting rows whose query rows are spread over several workgroups,
+uneven draft rows per request through row_sel) and the two-launch fallback
+(large grids, one row with more heads than a workgroup holds, slices past
+the LDS bitmap), rows with fewer than k blocks, rows with nothing scored, and
+rows whose threshold bin holds more candidates than the LDS (massive ties).
+Each case also asserts which of the two paths the library takes.
 """
 import numpy as np
 import pytest
 import torch
 
+from block_sparse_attention_qsa_amd import api
 from block_sparse_attention_qsa_amd.pipeline import QSALayer, QSAPrefill
 from block_sparse_attention_qsa_amd.workloads import (SHAPE_FP8, SHAPE_MAIN, SHAPE_TINY, QSAShape, make_prefill_workload,
                                                       make_workload, named_workload)
@@ -25,10 +28,13 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _pair(wl, P, cls=QSALayer, **kw):
+def _pair(wl, P, cls=QSALayer, launches=None, **kw):
     a = cls(wl, P, poison=True, **kw)
     b = cls(wl, P, poison=True, select_decode=False, **kw)
     assert a.select_decode and not b.select_decode
+    if launches is not None:  # which path the call takes (one kernel, or the finalize then the attention)
+        got = api.qsa_select_sparse_decode_launches(a.cfg, wl.num_sel, wl.q_per_sel, P, a.max_seq_len)
+        assert got == launches, f"expected {launches} launch(es), the library takes {got}"
     for layer in (a, b):
         layer.prefill()
         layer.step()
@@ -41,7 +47,8 @@ def _same(a, b):
     sh = a.wl.shape
     if a.wl.q_per_sel * (sh.num_q_heads // sh.num_kv_heads) > 16:
         # the separate decode then runs 4-wave workgroups (a different summation
-        # order over the tiles): both are checked against the oracle instead
+        # order over the tiles) while the fused kernel spreads the rows over
+        # 8-wave row groups: both are checked against the oracle instead
         check_layer(b.wl, b)
         return
     assert torch.equal(a.o_part, b.o_part), "o_part differs from the separate calls"
@@ -50,44 +57,63 @@ def _same(a, b):
 
 
 CASES = [
-    # (name, shape, lengths, q_per_sel, P, seed)
-    ("main-mixed", SHAPE_MAIN, [70001, 9000, 2049, 13, 4, 3, 600, 40000], 1, 4, 401),
-    ("main-p16", SHAPE_MAIN, [65536, 30000], 1, 16, 402),
-    ("main-qps2", SHAPE_MAIN, [20001, 5000, 3], 2, 2, 403),   # 16 heads x d=128: two row groups
-    ("g16-fallback", QSAShape(16, 1, 128, 64, 512, 64), [20001, 5000, 3], 1, 2, 418),  # 16 heads per KV head: two launches
-    ("tiny-qps4", SHAPE_TINY, [3001, 100, 17, 2], 4, 3, 404),           # 4 heads x 4 rows, d=64
-    ("d64-g8-qps2", QSAShape(16, 2, 64, 128, 64, 32), [12000, 777], 2, 5, 405),
-    ("fp8", SHAPE_FP8, [50000, 1234, 9], 1, 8, 406),
-    ("k7-short", QSAShape(8, 2, 64, 32, 7, 16), [3, 17, 27, 28, 29, 100, 1000], 1, 2, 407),
-    ("fp8-d64-qps2", QSAShape(16, 2, 64, 64, 512, 64, kv_dtype="fp8"), [30000, 4099, 2], 2, 4, 408),
-    ("page128", QSAShape(16, 2, 128, 64, 512, 128), [50001, 777, 12345], 1, 8, 409),
-    ("k2048", QSAShape(16, 2, 128, 64, 2048, 64), [20000, 9003, 5000], 1, 4, 410),   # the largest k
-    ("p1", SHAPE_MAIN, [40000, 3001, 2], 1, 1, 411),          # one split
-    ("p32", SHAPE_MAIN, [90001, 20000, 7, 64], 1, 32, 412),   # 32 splits (two rounds of the merge's loads)
+    # (name, shape, lengths, q_per_sel, P, seed, launches)
+    ("main-mixed", SHAPE_MAIN, [70001, 9000, 2049, 13, 4, 3, 600, 40000], 1, 4, 401, 1),
+    ("main-p16", SHAPE_MAIN, [65536, 30000], 1, 16, 402, 1),
+    ("main-qps2", SHAPE_MAIN, [20001, 5000, 3], 2, 2, 403, 1),      # 16 heads x d=128: two row groups
+    ("g16-fallback", QSAShape(16, 1, 128, 64, 512, 64), [20001, 5000, 3], 1, 2, 418, 2),  # 16 heads at d=128
+    ("g16-d64", QSAShape(16, 1, 64, 64, 512, 64), [20001, 5000, 3], 1, 2, 420, 1),      # 16 heads at d=64
+    ("g32-fallback", QSAShape(32, 1, 64, 64, 512, 64), [20001, 5000, 3], 1, 2, 419, 2),  # 32 heads of one row
+    ("tiny-qps4", SHAPE_TINY, [3001, 100, 17, 2], 4, 3, 404, 1),           # 4 heads x 4 rows, d=64
+    ("d64-g8-qps2", QSAShape(16, 2, 64, 128, 64, 32), [12000, 777], 2, 5, 405, 1),
+    ("fp8", SHAPE_FP8, [50000, 1234, 9], 1, 8, 406, 1),
+    ("k7-short", QSAShape(8, 2, 64, 32, 7, 16), [3, 17, 27, 28, 29, 100, 1000], 1, 2, 407, 1),
+    ("fp8-d64-qps2", QSAShape(16, 2, 64, 64, 512, 64, kv_dtype="fp8"), [30000, 4099, 2], 2, 4, 408, 1),
+    ("page128", QSAShape(16, 2, 128, 64, 512, 128), [50001, 777, 12345], 1, 8, 409, 1),
+    ("k2048", QSAShape(16, 2, 128, 64, 2048, 64), [20000, 9003, 5000], 1, 4, 410, 1),   # the largest k
+    ("p1", SHAPE_MAIN, [40000, 3001, 2], 1, 1, 411, 1),          # one split
+    ("p32", SHAPE_MAIN, [90001, 20000, 7, 64], 1, 32, 412, 1),   # 32 splits (two rounds of the merge's loads)
     # 4 query rows x 8 heads = 32 heads per selecting row, more than one fused workgroup holds:
-    # two or four workgroups per KV head, each with its own query rows
-    ("fp8-qps4-rowgroups", SHAPE_FP8, [70003, 9001, 4], 4, 4, 415),
-    ("bf16-qps2-rowgroups", SHAPE_MAIN, [30001, 6002], 2, 8, 416),
-    ("d64-qps4-rowgroups", QSAShape(16, 2, 64, 64, 512, 64), [40003, 5001], 4, 3, 417),
-    # 16-token pages: row 0 spans 5,001 pages, more than the LDS page-table copy (looked up in global memory)
-    ("page16-long", QSAShape(16, 2, 128, 64, 512, 16), [80001, 5000, 65536], 1, 4, 414),
+    # several row groups per KV head, each with its own query rows
+    ("fp8-qps4-rowgroups", SHAPE_FP8, [70003, 9001, 4], 4, 4, 415, 1),
+    ("bf16-qps2-rowgroups", SHAPE_MAIN, [30001, 6002], 2, 8, 416, 1),
+    ("d64-qps4-rowgroups", QSAShape(16, 2, 64, 64, 512, 64), [40003, 5001], 4, 3, 417, 1),
+    # 16-token pages: row 0 spans 18,751 pages, more than the LDS page-table copy (looked up in global memory)
+    ("page16-long", QSAShape(16, 2, 128, 64, 512, 16), [300001, 5000, 65536], 1, 2, 414, 1),
 ]
 
 
-@pytest.mark.parametrize("name,shape,lens,qps,P,seed", CASES, ids=[c[0] for c in CASES])
-def test_select_decode_matches_oracle_and_separate_calls(name, shape, lens, qps, P, seed):
+@pytest.mark.parametrize("name,shape,lens,qps,P,seed,launches", CASES, ids=[c[0] for c in CASES])
+def test_select_decode_matches_oracle_and_separate_calls(name, shape, lens, qps, P, seed, launches):
     wl = make_workload(shape, lens, q_per_sel=qps, seed=seed, device=DEV, name=f"seldec-{name}")
     say(f"[gpu] select+decode {name} S={wl.num_sel} R={wl.num_rows} P={P}")
-    a, b = _pair(wl, P)
+    a, b = _pair(wl, P, launches=launches)
     check_layer(wl, a)
     _same(a, b)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_uneven_draft_rows_through_row_sel(kv):
+    """Requests carry 1, 3, 0, 4, 2 and 5 draft tokens: one query row each, all
+    sharing the selection of their request's first one (row_sel), with their
+    own tails; an idle request has no rows.  One call, against the oracle and
+    the separate calls."""
+    shape = QSAShape(16, 2, 128, 64, 512, 64, kv_dtype=kv)
+    wl = make_workload(shape, [40007, 9001, 5000, 70001, 2050, 30000], rows_per_req=[1, 3, 0, 4, 2, 5],
+                       seed=421, device=DEV, name=f"seldec-uneven-{kv}")
+    assert wl.num_sel == 5 and wl.num_rows == 15 and wl.q_per_sel == 5
+    say(f"[gpu] uneven draft rows {kv}: S={wl.num_sel} R={wl.num_rows}")
+    a, b = _pair(wl, 4, launches=1)
+    check_layer(wl, a)
+    check_layer(wl, b)
+    assert torch.equal(a.topk, b.topk)
 
 
 def test_select_decode_large_grid_uses_two_launches():
     """64 selecting rows x 2 KV heads x 4 splits = 512 workgroups: the fallback path."""
     lens = [3000 + 97 * i for i in range(64)]
     wl = make_workload(SHAPE_MAIN, lens, seed=31, device=DEV, name="seldec-grid512")
-    a, b = _pair(wl, 4)
+    a, b = _pair(wl, 4, launches=2)
     check_layer(wl, a)
     _same(a, b)
 
@@ -149,7 +175,7 @@ def test_select_decode_prefill_rows():
 def test_select_decode_named_decode_batch():
     """The 32-request decode batch (scaled): 32 rows x 2 heads x 4 splits = 256 workgroups, one launch."""
     wl = named_workload(2, device=DEV, scale_ctx=1 / 8)
-    a, b = _pair(wl, 4)
+    a, b = _pair(wl, 4, launches=1)
     check_layer(wl, a)
     _same(a, b)
 
@@ -158,8 +184,9 @@ def test_select_decode_rows_beyond_the_lds_bitmap():
     """max_seq_len above 1,048,576 tokens: the selection keeps its bitmap in the
     workspace (rows of up to 4M blocks), and the call takes the two-launch path."""
     wl = make_workload(SHAPE_MAIN, [70001, 9000, 13], seed=44, device=DEV, name="seldec-bigrows")
-    a = QSALayer(wl, 4, poison=True, max_seq_len=1_200_000)
-    b = QSALayer(wl, 4, poison=True, max_seq_len=1_200_000, select_decode=False)
+    a = QSALayer(wl, 2, poison=True, max_seq_len=1_200_000)
+    b = QSALayer(wl, 2, poison=True, max_seq_len=1_200_000, select_decode=False)
+    assert api.qsa_select_sparse_decode_launches(a.cfg, wl.num_sel, 1, 2, 1_200_000) == 2
     for layer in (a, b):
         layer.prefill()
         layer.step()

@@ -172,22 +172,23 @@ def test_front_end_swapped_gains_is_caught(monkeypatch):
     assert _fails(FP.test_composed_front_end_at_position_zero)
 
 
-def test_split_by_position_in_the_selection_is_caught(monkeypatch):
-    """The split rule of runs of the ascending selection (not slices of the context)."""
+def test_split_by_fixed_context_slices_is_caught(monkeypatch):
+    """The rule of fixed slices of the context (not runs of the selection)."""
     def bad(blocks, sel_seq_len, row_seq_len, num_splits):
         b = np.asarray(blocks, dtype=np.int64)
         b = np.sort(b[b >= 0])
-        n, parts = b.shape[0], []
+        nb, parts = sel_seq_len // 4, []
         for p in range(num_splits):
-            lo, hi = (p * n) // num_splits, ((p + 1) * n) // num_splits
-            toks = (b[lo:hi, None] * 4 + np.arange(4)[None, :]).reshape(-1)
+            lo, hi = (p * nb) // num_splits, ((p + 1) * nb) // num_splits
+            mine = b[(b >= lo) & (b < hi)]
+            toks = (mine[:, None] * 4 + np.arange(4)[None, :]).reshape(-1)
             if p == num_splits - 1:
                 toks = np.concatenate([toks, np.arange(O.tail_start(sel_seq_len), row_seq_len)])
             parts.append(toks)
         return parts
     monkeypatch.setattr(O, "split_token_positions", bad)
-    assert _fails(P.test_split_worked_example_slices_of_the_context)
-    assert _fails(P.test_split_parts_stay_inside_their_context_slices, 700)
+    assert _fails(P.test_split_worked_example_runs_of_the_selection)
+    assert _fails(P.test_split_parts_are_balanced_contiguous_runs, 700)
 
 
 def test_rows_ignoring_row_sel_is_caught(monkeypatch):
