@@ -50,6 +50,7 @@ SIGNATURES = {
     "qsa_index_topk_workspace_size": (ctypes.c_size_t, [_CFG, _I, _I]),
     "qsa_index_topk_workspace_init": (_I, [_P, ctypes.c_size_t, _P]),
     "qsa_index_topk": (_I, [_CFG, _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "qsa_index_topk_noalloc": (_I, [_CFG, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "qsa_compress_index_topk": (_I, [_CFG, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P,
                                      ctypes.c_size_t, _P]),
     "qsa_prefill_index_topk": (_I, [_CFG, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),

@@ -121,6 +121,19 @@ def qsa_index_topk(cfg: QSAConfig, q_index: torch.Tensor, sel_req: torch.Tensor,
                                       workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def qsa_index_topk_noalloc(cfg: QSAConfig, q_index: torch.Tensor, sel_req: torch.Tensor,
+                           sel_seq_len: torch.Tensor, block_table: torch.Tensor, ckey_cache: torch.Tensor,
+                           topk: torch.Tensor, max_seq_len: int, stream=None) -> None:
+    """qsa_index_topk over the library's own device scratch (no workspace argument, no allocation)."""
+    _dt(q_index, torch.int8); _dt(ckey_cache, torch.int8); _dt(topk, torch.int32)
+    _dt(sel_req, torch.int32); _dt(sel_seq_len, torch.int32); _dt(block_table, torch.int32)
+    c = cfg.to_c()
+    S = sel_req.shape[0]
+    _check(_lib.load().qsa_index_topk_noalloc(ctypes.byref(c), S, int(max_seq_len), _ptr(q_index), _ptr(sel_req),
+                                              _ptr(sel_seq_len), _ptr(block_table), _ptr(ckey_cache), _ptr(topk),
+                                              _stream(stream)))
+
+
 def qsa_compress_index_topk(cfg: QSAConfig, new_keys: torch.Tensor, new_cu: torch.Tensor,
                             seq_len_before: torch.Tensor, ring: torch.Tensor, q_index: torch.Tensor,
                             sel_req: torch.Tensor, sel_seq_len: torch.Tensor, block_table: torch.Tensor,

@@ -136,6 +136,32 @@ qsa_status qsa_index_topk(const qsa_config* cfg, int32_t num_sel_rows, int32_t m
                            block_table, ckey_cache, topk, lay, workspace, stream);
 }
 
+qsa_status qsa_index_topk_noalloc(const qsa_config* cfg, int32_t num_sel_rows, int32_t max_seq_len,
+                                  const int8_t* q_index, const int32_t* sel_req, const int32_t* sel_seq_len,
+                                  const int32_t* block_table, const int8_t* ckey_cache, int32_t* topk,
+                                  hipStream_t stream) {
+  qsa_status st = check_config(cfg, true, false);
+  if (st != QSA_OK) return st;
+  if (num_sel_rows < 0 || num_sel_rows > 65535)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "num_sel_rows must be in [0, 65535] (got %d)", num_sel_rows);
+  if (max_seq_len < 0 || max_seq_len > QSA_MAX_SEQ_LEN)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "max_seq_len must be in [0, %d] (got %d)", QSA_MAX_SEQ_LEN, max_seq_len);
+  if (num_sel_rows == 0) return QSA_OK;
+  if (!q_index || !sel_req || !sel_seq_len || !block_table || !ckey_cache || !topk)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_index_topk_noalloc: NULL array argument");
+  if (!aligned(ckey_cache, 16) || !aligned(q_index, 4))
+    return fail(QSA_ERR_INVALID_ARGUMENT,
+                "qsa_index_topk_noalloc: ckey_cache needs 16-byte, q_index 4-byte alignment");
+  const size_t need = topk_workspace_layout(num_sel_rows, max_seq_len).total;
+  if (need > (size_t)QSA_NOALLOC_SCRATCH_BYTES)
+    return fail(QSA_ERR_WORKSPACE,
+                "qsa_index_topk_noalloc: %d rows of up to %d tokens need %zu bytes of scratch, more than the "
+                "library's %zu; use qsa_index_topk with a workspace of qsa_index_topk_workspace_size bytes",
+                num_sel_rows, max_seq_len, need, (size_t)QSA_NOALLOC_SCRATCH_BYTES);
+  return launch_index_topk_noalloc(*cfg, num_sel_rows, max_seq_len, q_index, sel_req, sel_seq_len, block_table,
+                                   ckey_cache, topk, stream);
+}
+
 qsa_status qsa_compress_index_topk(const qsa_config* cfg, int32_t num_reqs, int32_t max_new_tokens,
                                    const int8_t* new_keys, const int32_t* new_cu,
                                    const int32_t* seq_len_before, int8_t* ring,

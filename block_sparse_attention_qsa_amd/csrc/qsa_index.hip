@@ -31,6 +31,8 @@
 //            padded with -1.  The workspace holds two histograms: a scan adds
 //            into the one its call count picks, and the selection clears the
 //            other, so the workspace stays clean between calls.
+#include <mutex>
+
 #include "qsa_append.h"
 #include "qsa_device.h"
 #include "qsa_internal.h"
@@ -717,6 +719,57 @@ qsa_status launch_compress_index_topk(const qsa_config& c, int32_t num_reqs, con
   if (st != QSA_OK || topk == nullptr) return st;
   return launch_finalize(S, sel_seq_len, c.topk_blocks, max_seq_len, topk, ws, stream,
                          "qsa_compress_index_topk(finalize)");
+}
+
+// ---- the library's own scratch (qsa_index_topk_noalloc) ----
+// A file-scope device array: every GPU the library runs on holds its own copy
+// until the process ends.  Host code never passes its name to a kernel (on the
+// host it is only a stand-in); the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+namespace {
+static __device__ __align__(256) uint8_t scratch[QSA_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+qsa_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QSA_ERR_HIP, "qsa_index_topk_noalloc: hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(QSA_ERR_UNSUPPORTED, "qsa_index_topk_noalloc: device %d beyond the %d the library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(QSA_ERR_HIP, "qsa_index_topk_noalloc: hipGetSymbolAddress of the scratch failed: %s",
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QSA_OK;
+}
+
+qsa_status launch_index_topk_noalloc(const qsa_config& c, int32_t S, int32_t max_seq_len, const int8_t* q_index,
+                                     const int32_t* sel_req, const int32_t* sel_seq_len, const int32_t* block_table,
+                                     const int8_t* ckey, int32_t* topk, hipStream_t stream) {
+  if (S == 0) return QSA_OK;
+  const TopkWorkspace lay = topk_workspace_layout(S, max_seq_len);
+  void* ws = nullptr;
+  qsa_status st = noalloc_scratch(&ws);
+  if (st != QSA_OK) return st;
+  // The scratch keeps the last call's contents, whose layout may differ: the
+  // histograms and the call counters (everything the scan reads before it
+  // writes) are zeroed first, by a fill kernel.
+  st = launch_ws_clear(reinterpret_cast<char*>(ws) + lay.off_hist, lay.off_cinfo - lay.off_hist, stream);
+  if (st != QSA_OK) return st;
+  st = launch_ws_clear(reinterpret_cast<char*>(ws) + lay.off_gen, lay.total - lay.off_gen, stream);
+  if (st != QSA_OK) return st;
+  return launch_index_topk(c, S, max_seq_len, q_index, sel_req, sel_seq_len, block_table, ckey, topk, lay, ws,
+                           stream);
 }
 
 qsa_status launch_prefill_index_topk(const qsa_config& c, int32_t B, int32_t R, int32_t max_rows,

@@ -64,6 +64,11 @@ qsa_status launch_prefill_index_topk(const qsa_config& c, int32_t B, int32_t R, 
 
 qsa_status launch_ws_clear(void* ws, size_t bytes, hipStream_t stream);
 
+// qsa_index_topk over the library's own scratch (a file-scope device array).
+qsa_status launch_index_topk_noalloc(const qsa_config& c, int32_t S, int32_t max_seq_len, const int8_t* q_index,
+                                     const int32_t* sel_req, const int32_t* sel_seq_len, const int32_t* block_table,
+                                     const int8_t* ckey, int32_t* topk, hipStream_t stream);
+
 size_t indexer_project_workspace_bytes(int32_t T, int32_t H, int32_t D);
 
 qsa_status launch_indexer_project(int32_t T, int32_t H, int32_t D, const void* hidden, const int32_t* positions,

@@ -176,6 +176,29 @@ qsa_status qsa_index_topk(const qsa_config* cfg, int32_t num_sel_rows, int32_t m
                           void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * qsa_index_topk_noalloc -- qsa_index_topk without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The work space is
+ * the library's own device array of QSA_NOALLOC_SCRATCH_BYTES (16 MiB), one per
+ * GPU, held until the process ends; the call allocates and frees nothing.
+ *   Arguments and results as qsa_index_topk, except that topk is required.
+ *   The scratch is shared by every call on a GPU and keeps the last call's
+ *   contents (each call first zeroes the part it reads before writing, with a
+ *   fill kernel): calls that overlap on one GPU race, so order them (one
+ *   stream, or synchronised).  Sizes: qsa_index_topk_workspace_size(cfg,
+ *   num_sel_rows, max_seq_len) must not exceed the scratch (for example 12
+ *   selecting rows of 262,144 tokens fit).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (index_dim), WORKSPACE (too large for
+ *         the scratch), HIP.
+ */
+#define QSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+qsa_status qsa_index_topk_noalloc(const qsa_config* cfg, int32_t num_sel_rows, int32_t max_seq_len,
+                                  const int8_t* q_index, const int32_t* sel_req, const int32_t* sel_seq_len,
+                                  const int32_t* block_table, const int8_t* ckey_cache, int32_t* topk,
+                                  hipStream_t stream);
+
+/*
  * qsa_compress_index_topk -- qsa_compress followed by qsa_index_topk, in one
  * scan launch (plus the selection), for decode-sized appends.  [QSA-DCP]: each
  * decode step appends the new tokens' keys to the compressed side cache and

@@ -98,6 +98,21 @@ def test_workspace_size_and_checks(lib):
     assert lib.qsa_index_topk_workspace_init(None, 100, None) == 3
 
 
+def test_index_topk_noalloc_rejects(lib):
+    c = cfg()
+
+    def na(S=8, L=65536, q=FAKE, topk=FAKE, **kw):
+        return lib.qsa_index_topk_noalloc(ctypes.byref(kw.get("c", c)), S, L, q, FAKE, FAKE, FAKE, FAKE, topk, None)
+    assert na(topk=None) == 1                      # the selection is required
+    assert na(q=None) == 1
+    assert na(S=-1) == 1
+    assert na(L=_lib.QSA_MAX_SEQ_LEN + 4) == 1
+    assert na(c=cfg(index_dim=96)) == 2
+    assert na(S=64, L=262144) == 3                 # more than the library's scratch
+    assert lib.qsa_index_topk_workspace_size(ctypes.byref(c), 12, 262144) <= 16 << 20   # the documented fit
+    assert na(S=0) == 0
+
+
 def test_prefill_index_topk_rejects(lib):
     c = cfg()
     n = lib.qsa_index_topk_workspace_size(ctypes.byref(c), 64, 65536)
