@@ -18,9 +18,10 @@ step is captured once in a HIP graph and replayed; timing uses HIP events on
 the capture stream.  Inputs are seeded synthetic data resident in HBM.
 
 Printed: one JSON line with the throughput in query rows per second, the
-roofline of the dominant kernel (the compressed-key scan of qsa_index_topk,
-timed with HIP events around its own launches) and the CPU oracle's rate on a
-bounded sample of the same workload.
+roofline of each of the step's three kernels (scan, selection + attention,
+merge: algorithmic bytes over the average launch time, HIP events on the
+launch stream) with the slowest of them as `roofline`, and the CPU oracle's
+rate on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -49,15 +50,17 @@ DESCR = {
 }
 
 
-def algorithmic_bytes(wl):
-    """Bytes the step must move, per layer (intermediates excluded).
+def algorithmic_parts(wl, num_splits: int):
+    """Bytes the step must move, per layer, by part.
 
     scan: every closed micro-block of every selecting row at its stored width
     (10 bits per index dim: D + D/4 bytes), its page-table entries and the
     indexer query;
-    attend: the selected and tail K/V rows of each selecting row's request,
-    read once per KV head for all rows sharing the selection (+ fp8 scales),
-    q, the output (fp32) and lse.
+    kv: the selected and tail K/V rows of each selecting row's request, read
+    once per KV head for all rows sharing the selection (+ fp8 scales);
+    q: the attention queries; out: the fp32 output and LSE;
+    part: the split partials (fp32 o_part + lse_part), written by the attention
+    and read by the merge (an intermediate: not in the step's bytes).
     """
     s = wl.shape
     D, page, d, hkv, hq = s.index_dim, s.page_size, s.head_dim, s.num_kv_heads, s.num_q_heads
@@ -67,16 +70,64 @@ def algorithmic_bytes(wl):
     row_sel = wl.row_sel.cpu().numpy()
     nb = sel_len // 4
     scan = int((nb * (D + D // 4)).sum() + (((sel_len + page - 1) // page) * 4).sum() + len(sel_len) * D)
-    attend = 0
+    kv = 0
     for si in range(wl.num_sel):
         rows = row_len[row_sel == si]
         if rows.size == 0:
             continue
         ntok = 4 * min(s.topk_blocks, int(nb[si])) + max(0, int(rows.max()) - 4 * int(nb[si]))
-        attend += ntok * hkv * d * esz * 2 + (ntok * 4 * 2 if s.kv_dtype == "fp8" else 0)
+        kv += ntok * hkv * d * esz * 2 + (ntok * 4 * 2 if s.kv_dtype == "fp8" else 0)
     R = wl.num_rows
-    attend += R * hq * d * 2 + R * hq * d * 4 + R * hq * 4
-    return scan, attend
+    return {"scan": scan, "kv": kv, "q": R * hq * d * 2, "out": R * hq * d * 4 + R * hq * 4,
+            "part": num_splits * R * hq * (d + 1) * 4}
+
+
+def kernel_times(layers, stream, iters: int):
+    """Average launch time (ms) of the step's scan, attention and merge calls,
+    from graphs of those calls over all layers, replayed `iters` times and timed
+    with HIP events on the launch stream."""
+    import torch
+
+    from block_sparse_attention_qsa_amd import api
+
+    def first(layer):
+        sel = not layer.select_decode
+        if layer.fused:
+            layer.compress_index(stream, select=sel)
+        else:
+            layer.compress(stream)
+            layer.index(stream, select=sel)
+
+    def second(layer):
+        if layer.select_decode:
+            layer.select_attend(stream)
+        else:
+            layer.decode(stream)
+
+    def timed(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            for _ in range(iters):
+                g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return a.elapsed_time(b) / (iters * len(layers))
+
+    both = timed(lambda: [(first(l), second(l)) for l in layers])
+    merge = timed(lambda: [l.merge(stream) for l in layers])
+    scan = timed(lambda: [first(l) for l in layers])
+    for layer in layers:  # scans without a selection leave their histograms summed: start clean
+        api.qsa_index_topk_workspace_init(layer.workspace, stream=stream)
+    torch.cuda.synchronize()
+    return {"scan": scan, "attention": both - scan, "merge": merge}
 
 
 def append_bytes(wl):
@@ -259,19 +310,28 @@ def stream_at_size(stream, nbytes: int, nbuf: int, iters: int):
             "bytes": n, "avg_launch_us": us, "GBps": n / (us * 1e-6) / 1e9, "frac_of_peak": n / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
-def measured_traffic(fused: bool):
-    """HBM bytes per scan launch from the committed rocprofv3 counter summary,
-    or None when the kernel source has changed since the counters were taken
-    (or they were taken for the other variant of the scan)."""
+COUNTER_FILES = {"scan": "score_kernel_long256k_hbm_counters.md",
+                 "attention": "select_decode_kernel_long256k_hbm_counters.md"}
+
+
+def measured_traffic(name: str, fused: bool, select_fused: bool, cfg: int):
+    """HBM bytes per launch of kernel `name` from its committed rocprofv3
+    counter summary (workload 3 only), or None when there is none, when the
+    kernel source has changed since the counters were taken, or when they were
+    taken for another variant of the step."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "score_kernel_long256k_hbm_counters.md")
+    if cfg != 3 or name not in COUNTER_FILES:
+        return None
+    path = os.path.join(ROOT, "profiles", COUNTER_FILES[name])
+    want = {"scan": "fused" if fused else "separate",
+            "attention": "fused" if select_fused else "separate"}[name]
     try:
         kv = dict(line.split(" = ", 1) for line in open(path).read().splitlines() if " = " in line)
-        if kv.get("variant", "separate").strip() != ("fused" if fused else "separate"):
+        if kv.get("variant", "separate").strip() != want:
             return None
         h = hashlib.sha256()
-        for name in kv["kernel_sources"].split(","):  # the scan kernel's file and the headers it includes
-            h.update(open(os.path.join(ROOT, name.strip()), "rb").read())
+        for src in kv["kernel_sources"].split(","):  # the kernel's file and the headers it includes
+            h.update(open(os.path.join(ROOT, src.strip()), "rb").read())
         if h.hexdigest() != kv["kernel_sources_sha256"].strip():
             return None
         return float(kv["traffic_bytes_per_launch"])
@@ -534,49 +594,43 @@ def main():
     marks = [e0] + evs + [e1]
     per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
 
-    # Dominant kernel: the compressed-key scan, as the step runs it (with the
-    # step's append when fused; topk=None runs only the scan kernel; re-appending
-    # the same tokens rewrites the same bytes).  Its launches for all layers, back
-    # to back, are captured in a graph and timed with HIP events on the launch
-    # stream; the layers rotate, so every launch streams its own (cold) cache.
-    fused = layers[0].fused
+    # Per-kernel timing, in the step's own launch sequence: each layer's step is
+    # three launches (scan, selection + attention, merge).  Graphs of (a) every
+    # layer's scan + attention call, (b) every layer's merge and (c) every
+    # layer's scan alone are replayed and timed with HIP events on the launch
+    # stream; the attention call's time is (a) - (c).  The layers rotate, so each
+    # launch reads its own cold data.  (c) runs last: scans without a selection
+    # in between add into the same histogram, so the workspaces are reset after it.
+    kt = kernel_times(layers, stream, args.kernel_iters) if args.kernel_iters > 0 else None
 
-    def scan_all():
-        for layer in layers:
-            wl = layer.wl
-            if fused:
-                api.qsa_compress_index_topk(layer.cfg, layer.step_keys, layer.step_cu, layer.step_before,
-                                            layer.ring, wl.q_index, wl.sel_req, wl.sel_seq_len, wl.block_table,
-                                            layer.ckey, None, layer.workspace, layer.step_max_new,
-                                            layer.max_seq_len, stream=stream)
-            else:
-                api.qsa_index_topk(layer.cfg, wl.q_index, wl.sel_req, wl.sel_seq_len, wl.block_table,
-                                   layer.ckey, None, layer.workspace, layer.max_seq_len, stream=stream)
-    kern_ms, n_launches = float("nan"), 0
-    if args.kernel_iters > 0:
-        kgraph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(kgraph, stream=stream):
-            scan_all()
-        torch.cuda.synchronize()
-        kgraph.replay()
-        torch.cuda.synchronize()
-        ka = torch.cuda.Event(enable_timing=True)
-        kb = torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            ka.record(stream)
-            for _ in range(args.kernel_iters):
-                kgraph.replay()
-            kb.record(stream)
-        torch.cuda.synchronize()
-        n_launches = args.kernel_iters * len(layers)
-        kern_ms = ka.elapsed_time(kb) / n_launches
-
-    scan_b, attend_b = zip(*[algorithmic_bytes(l.wl) for l in layers])
+    parts = [algorithmic_parts(l.wl, P) for l in layers]
     app_b = [append_bytes(l.wl) for l in layers]
-    scan_per_launch = float(np.mean(scan_b)) + (float(np.mean(app_b)) if fused else 0.0)
-    step_bytes = float(sum(scan_b) + sum(attend_b) + sum(app_b))
-    achieved = scan_per_launch / (kern_ms * 1e-3) / 1e9
+    fused = layers[0].fused
+    per = {k: float(np.mean([x[k] for x in parts])) for k in parts[0]}
+    step_bytes = float(sum(x["scan"] + x["kv"] + x["q"] + x["out"] for x in parts) + sum(app_b))
     rows_s = rows_per_step / (ms * 1e-3)
+    sel_fused = layers[0].select_decode
+    kernels = {
+        "scan": {"kernel": ("qsa::score_kernel<D, true> (qsa_compress_index_topk: append + compressed-key scan)"
+                            if fused else "qsa::score_kernel<D, false> (qsa_index_topk compressed-key scan)")
+                 + ("" if sel_fused else " + qsa::finalize_kernel"),
+                 "bytes_per_launch": per["scan"] + (float(np.mean(app_b)) if fused else 0.0),
+                 "bytes": "compressed keys of every closed block at 10 bits per dim, page-table entries, "
+                          "indexer query" + (", the append" if fused else "")},
+        "attention": {"kernel": ("qsa::select_decode_kernel (selection + sparse attention)" if sel_fused
+                                 else "qsa::decode_kernel (sparse attention)"),
+                      "bytes_per_launch": per["kv"] + per["q"] + per["part"],
+                      "bytes": "selected + tail K/V rows once per KV head (+ fp8 scales), q, "
+                               "the split partials written"},
+        "merge": {"kernel": "qsa::merge_kernel", "bytes_per_launch": per["part"] + per["out"],
+                  "bytes": "split partials read, fp32 output and LSE written"},
+    }
+    for name, kd in kernels.items():
+        us = kt[name] * 1e3 if kt else float("nan")
+        ach = kd["bytes_per_launch"] / (us * 1e-6) / 1e9
+        kd.update({"bound": "hbm", "avg_launch_us": us, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(name, fused, sel_fused, cfg)})
+    dom = max(kernels, key=lambda n: kernels[n]["avg_launch_us"] if kt else 0.0)
 
     res = {
         "metric": METRIC,
@@ -596,26 +650,23 @@ def main():
         "config": {"workload": f"cfg{cfg} {DESCR[cfg]}", "layers_per_step": args.layers,
                    "query_rows_per_layer": wl0.num_rows, "splits": P, "hip_graph": graph is not None,
                    "append": "fused into the scan" if fused else "separate qsa_compress launch",
-                   "selection": ("with the attention (qsa_select_sparse_decode)" if layers[0].select_decode
+                   "selection": ("with the attention (qsa_select_sparse_decode)" if sel_fused
                                  else "separate finalize launch"),
                    "index_arith": "int8 dot4 -> int32 (exact)", "attention_arith": "bf16 MFMA / fp32 softmax"},
         "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
                      "frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "wall_s": t_wall},
-        "roofline": {"kernel": ("qsa::score_kernel<D, true> (qsa_compress_index_topk: append + compressed-key scan)"
-                                if fused else "qsa::score_kernel<D, false> (qsa_index_topk compressed-key scan)"),
-                     "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(fused) if cfg == 3 else None,
-                     "bytes_per_launch": scan_per_launch, "avg_launch_us": kern_ms * 1e3,
-                     "launches_timed": n_launches},
+        # the kernel with the longest average launch of the step's three
+        "roofline": dict(kernels[dom], name=dom, launches_timed=args.kernel_iters * len(layers)),
+        "kernels": kernels,
     }
+    if kt:
+        res["kernels_sum_us_per_layer"] = sum(kt.values()) * 1e3
     res["stream_ceiling"] = stream_ceiling(stream)
     if args.kernel_iters > 0:
         # a bare stream of the scan's size: the rate a transfer this short reaches at all
-        same = stream_at_size(stream, int(scan_per_launch), len(layers), args.kernel_iters)
-        same["scan_frac_of_it"] = res["roofline"]["achieved"] / same["GBps"]
+        same = stream_at_size(stream, int(kernels["scan"]["bytes_per_launch"]), len(layers), args.kernel_iters)
+        same["scan_frac_of_it"] = kernels["scan"]["achieved"] / same["GBps"]
         res["stream_ceiling"]["at_scan_size"] = same
     if not args.no_cpu_baseline:
         procs = max(1, os.cpu_count() or 1)

@@ -187,7 +187,8 @@ struct Attend {
   };
 
   bf16x8 bq[NT][KK];
-  int rlen[NT];  // context length of the row owning head nt*16+lc (-1: padding)
+  int rlen_[NT];   // context length of the row owning head nt*16+lc, as loaded
+  bool real_[NT];  // head nt*16+lc is one of the group's (else padding: no token counts)
   float m_run[NT], l_run[NT];
   // O in the MFMA C layout: acc[nt][m][e] = O[head nt*16+4lg+e][d = (D/16) lc + m]
   f32x4 acc[NT][NM];
@@ -202,10 +203,16 @@ struct Attend {
     }
   }
 
+  // The context length of head nt*16+lc's row (-1: padding).  Padding is
+  // applied here, where the lengths are used, so that nothing waits for the
+  // loads of load_q before then.
+  __device__ __forceinline__ int rlen(int nt) const { return real_[nt] ? rlen_[nt] : -1; }
+
   // Q as the QK MFMA B operand: lane (lc, lg) holds head n = nt*16+lc, dims
-  // 32kk+8lg..+8.  Unconditional loads (padding heads read the first row's
-  // first head and are zeroed).  row_of_group(i): query row of the group's
-  // i-th row (-1: none).
+  // 32kk+8lg..+8.  Unconditional loads, used as loaded (padding heads read
+  // the first row's first head; their tokens are all masked through rlen, so
+  // their query values never count).  row_of_group(i): query row of the
+  // group's i-th row (-1: none).
   template <class RowFn>
   __device__ __forceinline__ void load_q(const DecodeArgs& a, int kvh, RowFn&& row_of_group) {
     const int lc = lane_id() & 15, lg = lane_id() >> 4;
@@ -219,13 +226,10 @@ struct Attend {
       const int r = real ? rr : r_first;
       const int h = kvh * a.G + (real ? n - i0 * a.G : 0);
       const uint16_t* qrow = a.q + ((size_t)r * a.Hq + h) * D;
-      const int rl = a.row_seq_len[r];
-      rlen[nt] = real ? rl : -1;
+      rlen_[nt] = a.row_seq_len[r];
+      real_[nt] = real;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const i32x4 v = ld16(qrow + 32 * kk + 8 * lg);
-        bq[nt][kk] = __builtin_bit_cast(bf16x8, real ? v : i32x4{0, 0, 0, 0});
-      }
+      for (int kk = 0; kk < KK; ++kk) bq[nt][kk] = __builtin_bit_cast(bf16x8, ld16(qrow + 32 * kk + 8 * lg));
     }
   }
 
@@ -235,7 +239,7 @@ struct Attend {
     if (p != a.P - 1) return 0;
     int tail_hi = 0;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) tail_hi = max(tail_hi, rlen[nt]);
+    for (int nt = 0; nt < NT; ++nt) tail_hi = max(tail_hi, rlen(nt));
     tail_hi = wave_max_i32(tail_hi);
     return (max(0, tail_hi - tail_lo) + 3) >> 2;
   }
@@ -385,7 +389,7 @@ struct Attend {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = cur.tok + e;
-        const bool ok = cur.tok >= 0 && t < rlen[nt];
+        const bool ok = cur.tok >= 0 && t < rlen(nt);
         float zz = c[nt][e] * a.scale_log2;
         if (FP8) zz *= cur.ks[e];
         z[e] = ok ? zz : -INFINITY;
@@ -584,7 +588,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeArgs a) {
 // row's selection itself from the scored workspace (RowSelector: the finalize
 // of select_row, into an LDS bitmap of the row) while the request's page-table
 // row is staged in LDS, then lists its own run of the ascending selection,
-// staged for the attention in the same pass, and attends it.  The row's top-k
+// stages it for the attention (one block per thread) and attends it.  The row's top-k
 // is never assembled in one place: the workgroups of row group 0 write their
 // runs of topk while the K/V loads are in flight.  No workgroup waits for
 // another: the row's histogram is only read (the workspace keeps two, and a
@@ -608,7 +612,10 @@ constexpr int kFusedHeads128 = 8, kFusedHeads64 = 16;
 static_assert(select_decode_ok<128, kFusedHeads128>() && !select_decode_ok<128, 2 * kFusedHeads128>() &&
               select_decode_ok<64, kFusedHeads64>(), "fused head limits");
 
-template <int D, int NH, bool FP8>
+// kIdent: no row map (row_sel null; row s is selecting row s, qg = qpw = 1).
+// A template parameter, not a branch: the hook then issues the same loads on
+// every path, and the compiler's waits count exactly the loads before them.
+template <int D, int NH, bool FP8, bool kIdent>
 __global__ __launch_bounds__(kFinThreads) void select_decode_kernel(DecodeArgs a, WsPtrs ws, int32_t max_seq_len,
                                                                      int32_t* __restrict__ topk_out) {
   static_assert(kFinThreads == 8 * 64, "the selection runs on the attention's 8 waves");
@@ -622,27 +629,30 @@ __global__ __launch_bounds__(kFinThreads) void select_decode_kernel(DecodeArgs a
   __shared__ float alpha_lds[8][At::NHP];
   const int p = blockIdx.x, kvh = (int)blockIdx.y / a.qg, g = (int)blockIdx.y % a.qg, s = blockIdx.z;
   const int w = threadIdx.x / 64;
-  const uint32_t t = ws.gen[0];  // the scan's histogram: t & 1
-  const int b = a.sel_req[s];
-  const int Lsel = max(a.sel_seq_len[s], 0);
-  asm volatile("" ::"s"(b), "s"(Lsel));  // scalar loads, issued now (a vector reload later would wait for the K/V)
+  int bv = 0;  // the request id, loaded behind the histogram (vector load, see RowSelector::first)
+  int b = 0, Lsel = 0;
   int btv[kBtPer];
   int nbt = 0, rs0 = -1;
   At at;
   at.init();
-  const bool ident = a.row_sel == nullptr;  // row s is selecting row s (qg = qpw = 1)
+  constexpr bool ident = kIdent;
+  RowSelector sel{sl, s, a.k, ws};
+  auto pre = [&] { bv = vload_same(a.sel_req + s); };
   // Issued after the selection's first loads: the request's page-table row
   // (up to kBtLds entries, past them the attention reads the table itself),
   // the first 64 entries of row_sel, and q with the row lengths when the rows
-  // are known without the row map.
+  // are known without the row map (waited for only where the attention uses
+  // them).
   auto hook = [&] {
+    b = __builtin_amdgcn_readfirstlane(bv);
+    Lsel = sel.Lsel;
     const int need = min((int)(((int64_t)Lsel + 8 + (1 << a.page_log2) - 1) >> a.page_log2), a.max_pages);
     nbt = min(need, kBtLds);
     const int32_t* btp = a.block_table + (size_t)b * a.max_pages;
 #pragma unroll
     for (int i = 0; i < kBtPer; ++i) btv[i] = btp[min((int)threadIdx.x + kFinThreads * i, max(nbt - 1, 0))];
-    rs0 = load_rs0(a);
-    if (ident) at.load_q(a, kvh, [&](int i) { return i == 0 ? s : -1; });
+    if constexpr (ident) at.load_q(a, kvh, [&](int i) { return i == 0 ? s : -1; });
+    else rs0 = load_rs0(a);
   };
   auto mid = [&] {
     find_rows(a, s, g, rs0, rows_lds);
@@ -652,11 +662,12 @@ __global__ __launch_bounds__(kFinThreads) void select_decode_kernel(DecodeArgs a
       if (e < nbt) bt_lds[e] = btv[i];
     }
   };
-  RowSelector sel{sl, s, a.k, ws};
-  sel.first(a.sel_seq_len, max_seq_len, t, hook, mid);
+  sel.first(a.sel_seq_len, max_seq_len, pre, hook, mid);
+  // rows_lds and bt_lds were written before the classification's barrier: the
+  // query rows of a row map go out now, waited for only at the first tile
+  if constexpr (!ident) at.load_q(a, kvh, [&](int i) { return rows_lds[i]; });
   sel.second();
-  // rows_lds and bt_lds were written before the classification's barrier
-  if (!ident) at.load_q(a, kvh, [&](int i) { return rows_lds[i]; });
+  const uint32_t t = sel.t;
   const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
   const BtView btv_lds{bt_lds, 0, nbt};
   const int ks = (int)sel.ks;
@@ -664,11 +675,15 @@ __global__ __launch_bounds__(kFinThreads) void select_decode_kernel(DecodeArgs a
   const int tail_lo = 4 * (Lsel >> 2);
   const int ntail = at.tail_blocks(a, p, tail_lo);
   typename At::Batch ba{list_a, i1 - i0, tail_lo, ntail, tok_a, pos_a, 0};
-  // The run's blocks are listed and staged in one pass (the tail's entries
-  // beside them: their positions are known in advance).
-  const int page_mask = (1 << a.page_log2) - 1;
-  auto put = [&](int i, int tok) {
-    if (i < kRound) {
+  // The run's blocks are listed (a barrier publishes the list), then staged
+  // with the tail's blocks, one entry per thread: the page ids missing from
+  // the LDS copy are then loaded all at once, not one after another.
+  sel.emit_run(i0, i1, list_a, [](int, int) {});
+  {
+    const int page_mask = (1 << a.page_log2) - 1;
+    const int nst = min(kRound, ba.total());
+    for (int i = threadIdx.x; i < nst; i += kFinThreads) {
+      const int tok = (i < ba.n) ? 4 * list_a[i] : tail_lo + 4 * (i - ba.n);
       const int pg = tok >> a.page_log2;
       int pid = bt_lds[min(pg, max(nbt - 1, 0))];
       asm volatile("" : "+v"(pid));  // keeps the two loads apart
@@ -676,10 +691,8 @@ __global__ __launch_bounds__(kFinThreads) void select_decode_kernel(DecodeArgs a
       tok_a[i] = tok;
       pos_a[i] = (pid << a.page_log2) | (tok & page_mask);
     }
-  };
-  for (int i = threadIdx.x; i < ntail; i += kFinThreads) put(ba.n + i, tail_lo + 4 * i);
-  sel.emit_run(i0, i1, list_a, [&](int i, int j) { put(i, 4 * j); });
-  if (sel.nb == 0) __syncthreads();  // (emit_run's barrier publishes the tail entries otherwise)
+  }
+  __syncthreads();
   // The issue runs unconditionally (a wave without a tile loads a masked row):
   // a branch around it would make the compiler wait for these loads where the
   // paths join.
@@ -831,8 +844,12 @@ template <int D, int NH, bool FP8>
 bool launch_select_decode_t(dim3 grid, const DecodeArgs& a, const WsPtrs& ws, int32_t max_seq_len,
                             int32_t* topk, hipStream_t stream) {
   if constexpr (select_decode_ok<D, NH>()) {
-    hipLaunchKernelGGL((select_decode_kernel<D, NH, FP8>), grid, dim3(kFinThreads), 0, stream, a, ws, max_seq_len,
-                       topk);
+    if (a.row_sel == nullptr)
+      hipLaunchKernelGGL((select_decode_kernel<D, NH, FP8, true>), grid, dim3(kFinThreads), 0, stream, a, ws,
+                         max_seq_len, topk);
+    else
+      hipLaunchKernelGGL((select_decode_kernel<D, NH, FP8, false>), grid, dim3(kFinThreads), 0, stream, a, ws,
+                         max_seq_len, topk);
     return true;
   } else {
     return false;

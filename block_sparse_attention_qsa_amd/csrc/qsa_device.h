@@ -21,6 +21,17 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 // 16-byte global load (dwordx4).
 __device__ __forceinline__ i32x4 ld16(const void* p) { return *reinterpret_cast<const i32x4*>(p); }
 
+// A dword every lane reads from the same address, as a vector load: it joins
+// the in-order queue of the wave's vector loads (waiting for it waits only for
+// the loads issued before it), where a scalar load would be waited for with
+// every other scalar load in flight.  The offset comes from an asm statement,
+// so the compiler cannot turn the load into a scalar one.
+__device__ __forceinline__ int32_t vload_same(const int32_t* p) {
+  int32_t z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return p[z];
+}
+
 // Agent-scope relaxed atomic accessors for counters shared between workgroups.
 __device__ __forceinline__ uint32_t ld_acq_u32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -106,10 +106,14 @@ __device__ __forceinline__ void load_hist_desc(const uint32_t* h, uint32_t (&cnt
 
 constexpr int kFinKeys = 8;  // candidate keys per finalize thread and round
 
-// Finalize threads per chunk in a round: as many as share the 512 threads, at
-// most kScoreChunk / kFinKeys (a round never reads past a chunk's list region).
+// Finalize threads per chunk in a round: as many as share the 512 threads with
+// every chunk of the widest row (one round of loads covers rows of up to 512
+// chunks), at most kScoreChunk / kFinKeys (a round never reads past a chunk's
+// list region).  Each chunk lists at least local_m = 4 x that many candidates,
+// so a row's lists hold about 2,048 candidates whatever its length: about four
+// times the blocks a top-512 takes from the row's average chunk.
 __device__ __forceinline__ int chunk_threads(int nb_stride) {
-  const int nch = min(nb_stride / kScoreChunk, 64);
+  const int nch = nb_stride / kScoreChunk;
   int t = 1;
   while (t * 2 * nch <= 512 && t * 2 * kFinKeys <= kScoreChunk) t *= 2;
   return t;
@@ -479,17 +483,23 @@ struct RowSelector {
   WsPtrs ws;
   // set by first()
   int nb = 0, nwords = 0, nchunks = 0, T = 0, tpc = 1, cpr = 1, sub = 0;
+  int Lsel = 0;     // the row's length (clamped at 0), uniform
+  uint32_t t = 0;   // the workspace's count of scored calls: the scan's histogram is t & 1
   uint32_t ks = 0, above = 0;
 
   __device__ __forceinline__ void mark(uint32_t j) {
     atomicOr(reinterpret_cast<unsigned long long*>(&L.bm[j >> 6]), 1ull << (j & 63));
   }
 
-  // The loads, the threshold bin and the classification.  hook(): once the
-  // first round of loads is in flight; mid(): by all threads right before the
-  // barrier that ends the classification.
-  template <class Hook, class Mid>
-  __device__ __forceinline__ void first(const int32_t* __restrict__ sel_seq_len, int32_t max_seq_len, uint32_t t,
+  // The loads, the threshold bin and the classification.  pre(): right after
+  // the histogram loads (the caller's first loads of its own); hook(): once
+  // the first round of loads is in flight (Lsel is then known); mid(): by all
+  // threads right before the barrier that ends the classification.  The row
+  // length and the count of scored calls are vector loads issued behind the
+  // histogram, so that nothing waits for a scalar round trip before the
+  // histogram goes out.
+  template <class Pre, class Hook, class Mid>
+  __device__ __forceinline__ void first(const int32_t* __restrict__ sel_seq_len, int32_t max_seq_len, Pre&& pre,
                                         Hook&& hook, Mid&& mid) {
     constexpr int kPer = kBins / kFinThreads;
     static_assert(kPer == 4 && kFinKeys == 8, "vector loads of the first round");
@@ -508,6 +518,9 @@ struct RowSelector {
     // cinfo and the first kFinKeys keys of its list.
     const uint4 hv0 = *reinterpret_cast<const uint4*>(ghist0 + kBins - 4 - 4 * tid);
     const uint4 hv1 = *reinterpret_cast<const uint4*>(ghist0 + ws.hist_stride + kBins - 4 - 4 * tid);
+    pre();
+    const int32_t Lv = vload_same(sel_seq_len + s);
+    const int32_t tv = vload_same(reinterpret_cast<const int32_t*>(ws.gen));
     int cc = min(tid / tpc, nchunks_max - 1);
     uint32_t ci = cinfo[cc];
     uint64_t kk[kFinKeys];
@@ -521,13 +534,15 @@ struct RowSelector {
       }
     };
     load_keys(cc);
-    const int Lr = sel_seq_len[s];
+    asm volatile("" ::: "memory");  // the loads go out here, not sunk to where they are used
+    // (one wait covers the histogram, the row length and the count: the key
+    // loads behind them are waited for only after the threshold)
+    const int Lr = __builtin_amdgcn_readfirstlane(Lv);
+    t = (uint32_t)__builtin_amdgcn_readfirstlane(tv);
+    Lsel = max(Lr, 0);
     hook();
-    asm volatile("" ::"s"(Lr));
     uint32_t hc[kPer];
     {
-      asm volatile("" ::"v"(hv0.x), "v"(hv0.y), "v"(hv0.z), "v"(hv0.w), "v"(hv1.x), "v"(hv1.y), "v"(hv1.z),
-                   "v"(hv1.w));
       const uint4 h = (t & 1u) ? hv1 : hv0;
       hc[0] = h.w; hc[1] = h.z; hc[2] = h.y; hc[3] = h.x;
     }
@@ -561,13 +576,12 @@ struct RowSelector {
         if (i < (uint32_t)kCandLds) L.cand[i] = key;
       }
     };
-    for (int c0 = 0; c0 < nchunks; c0 += cpr) {
+    // One round: the chunks c0 + tid / tpc, whose cinfo and first keys are in
+    // ci and kk.  The first round is a call of its own, outside the loop, so
+    // that its waits count only the loads issued before the hook's (a wait in
+    // a loop body shared with later rounds would wait for every load).
+    auto round = [&](int c0) {
       const int c = c0 + tid / tpc;
-      if (c0 > 0) {
-        cc = min(c, nchunks_max - 1);
-        ci = cinfo[cc];
-        load_keys(cc);
-      }
       uint32_t at_t = 0;
       if (c < nchunks) {
         const uint32_t cnt = ci >> 16;
@@ -600,6 +614,13 @@ struct RowSelector {
           pos += (at_t >> e) & 1u;
         }
       }
+    };
+    round(0);
+    for (int c0 = cpr; c0 < nchunks; c0 += cpr) {
+      cc = min(c0 + tid / tpc, nchunks_max - 1);
+      ci = cinfo[cc];
+      load_keys(cc);
+      round(c0);
     }
     mid();
     __syncthreads();
@@ -719,23 +740,42 @@ struct RowSelector {
   template <class Each>
   __device__ __forceinline__ void emit_run(int i0, int i1, int32_t* list, Each&& each) {
     if (nb == 0) return;
+    const int per = (nwords + kFinThreads - 1) / kFinThreads;  // <= kWordsLds / kFinThreads
+    if (per <= 2) emit_words<2>(per, i0, i1, list, each);
+    else emit_words<kWordsLds / kFinThreads>(per, i0, i1, list, each);
+  }
+
+  // emit_run with up to N bitmap words per thread, held in registers (read
+  // once for the popcounts; the walk then runs from registers).
+  template <int N, class Each>
+  __device__ __forceinline__ void emit_words(int per, int i0, int i1, int32_t* list, Each&& each) {
     const int tid = threadIdx.x;
-    const int per = (nwords + kFinThreads - 1) / kFinThreads;
-    const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
+    const int w0 = min(nwords, tid * per), nw = min(nwords, w0 + per) - w0;
+    uint64_t wv[N];
     uint32_t cntw = 0;
-    for (int i = w0; i < w1; ++i) cntw += (uint32_t)__popcll(L.bm[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      wv[i] = (i < nw) ? L.bm[min(w0 + i, kWordsLds - 1)] : 0ull;
+      cntw += (uint32_t)__popcll(wv[i]);
+    }
     uint32_t pos = block_excl_scan<kFinThreads, false>(cntw, L.sh);
     if ((int)pos < i1 && (int)(pos + cntw) > i0) {  // this thread's words hold part of the run
-      for (int i = w0; i < w1; ++i) {
-        uint64_t m = L.bm[i];
-        while (m) {
-          const int bit = __ffsll((long long)m) - 1;
-          m &= m - 1;
-          if ((int)pos >= i0 && (int)pos < i1) {
-            list[pos - i0] = i * 64 + bit;
-            each((int)pos - i0, i * 64 + bit);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        uint64_t m = wv[i];
+        const uint32_t c = (uint32_t)__popcll(m);
+        if ((int)(pos + c) > i0 && (int)pos < i1) {
+          while (m) {
+            const int bit = __ffsll((long long)m) - 1;
+            m &= m - 1;
+            if ((int)pos >= i0 && (int)pos < i1) {
+              list[pos - i0] = (w0 + i) * 64 + bit;
+              each((int)pos - i0, (w0 + i) * 64 + bit);
+            }
+            ++pos;
           }
-          ++pos;
+        } else {
+          pos += c;
         }
       }
     }
