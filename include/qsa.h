@@ -279,9 +279,11 @@ qsa_status qsa_prefill_index_topk(const qsa_config* cfg, int32_t num_reqs, int32
  *            row_sel[r] outside [0, num_sel_rows), and rows past the first
  *            max_rows_per_sel (in index order) of one selecting row, are not
  *            attended: their o_part / lse_part entries are not written.
- * Split p of P owns a slice of the selecting row's context: the selected
- * blocks j with floor(p*nb/P) <= j < floor((p+1)*nb/P), nb = floor(sel_seq_len/4);
- * split P-1 also owns the tail.  For query head h (KV head h / (H_q/H_kv)):
+ * Split p of P owns a contiguous stretch of the selecting row's context: the
+ * run of entries [floor(p*n/P), floor((p+1)*n/P)) of its n = min(k, nb)
+ * ascending selected blocks (nb = floor(sel_seq_len/4)), so every split takes
+ * a near-equal share of the selection; split P-1 also owns the tail.  For
+ * query head h (KV head h / (H_q/H_kv)):
  *   z_t = softmax_scale * q[r][h] . K_t   (fp8: times k_scale of token t)
  *   lse_part[p][r][h] = log sum_t exp(z_t)                 (natural log)
  *   o_part[p][r][h][:] = sum_t exp(z_t - lse) V_t          (fp8: V_t * v_scale_t)
