@@ -115,3 +115,87 @@ def test_composed_front_end_at_position_p():
     assert np.allclose(qf[0], want_q, atol=1e-12) and np.allclose(kf[0], want_k, atol=1e-12)
     assert qi[0].tolist() == np.clip(np.rint(want_q), -127, 127).astype(int).tolist()
     assert ki[0].tolist() == np.clip(np.rint(want_k), -127, 127).astype(int).tolist()
+
+
+# ---- MRoPE (F5): three position components, contiguous frequency sections ----
+
+def _unit(D, i):
+    e = np.zeros((1, D))
+    e[0, i] = 1.0
+    return e
+
+
+def test_mrope_with_equal_components_is_the_1d_rotation():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((4, 16))
+    p = np.array([0, 7, 4096, 999983])
+    assert np.array_equal(F.mrope(x, np.stack([p, p, p]), 10000.0, (2, 3, 3)), F.rope(x, p, 10000.0))
+
+
+def test_mrope_each_section_turns_with_its_own_component_only():
+    """D = 16, sections (2, 3, 3): pairs 0-1 follow the temporal component,
+    2-4 the height, 5-7 the width.  A position with one non-zero component
+    turns exactly that section's pairs, each by p * base^(-2i/D) (closed form)."""
+    D, base, p = 16, 10000.0, 11
+    sec = (2, 3, 3)
+    owner = [0, 0, 1, 1, 1, 2, 2, 2]
+    for c in range(3):
+        pos3 = np.zeros((3, 1), dtype=np.int64)
+        pos3[c, 0] = p
+        for i in range(D // 2):
+            y = F.mrope(_unit(D, i), pos3, base, sec)
+            a = p * base ** (-2.0 * i / D) if owner[i] == c else 0.0
+            want = np.zeros(D)
+            want[i], want[i + D // 2] = np.cos(a), np.sin(a)
+            assert np.allclose(y[0], want, rtol=0, atol=1e-12), (c, i)
+
+
+def test_mrope_first_pair_of_each_section_closed_form():
+    D, base = 64, 10000.0
+    sec = (8, 12, 12)
+    pos3 = np.array([[3], [5], [7]])
+    for i, p in [(0, 3), (8, 5), (20, 7)]:
+        y = F.mrope(_unit(D, i), pos3, base, sec)
+        a = p * base ** (-2.0 * i / D)
+        assert np.isclose(y[0, i], np.cos(a), atol=1e-12) and np.isclose(y[0, i + D // 2], np.sin(a), atol=1e-12)
+
+
+def test_mrope_keeps_pair_norms_and_depends_on_relative_positions_only():
+    rng = np.random.default_rng(6)
+    x, y = rng.standard_normal((1, 32)), rng.standard_normal((1, 32))
+    sec = (4, 6, 6)
+    m, n, d = np.array([[7], [30], [2]]), np.array([[3], [1], [50]]), np.array([[100], [-13], [4096]])
+    xm = F.mrope(x, m, 10000.0, sec)
+    assert np.allclose(xm[0, :16] ** 2 + xm[0, 16:] ** 2, x[0, :16] ** 2 + x[0, 16:] ** 2)
+    a = (xm @ F.mrope(y, n, 10000.0, sec).T).item()
+    b = (F.mrope(x, m + d, 10000.0, sec) @ F.mrope(y, n + d, 10000.0, sec).T).item()
+    assert np.isclose(a, b, rtol=0, atol=1e-8)
+
+
+def test_composed_front_end_with_mrope():
+    """The composed front end at position (p_t, p_h, p_w) with sections (1, 1, 2)
+    of D = 8: q = e_0 normalised lies in pair 0 (temporal) and turns by p_t; k = 2 e_1
+    lies in pair 1 (height) and turns by p_h * base^(-2/D)."""
+    rng = np.random.default_rng(4)
+    H, D, base = 16, 8, 10000.0
+    w = rng.standard_normal((2 * D, H))
+    w[:, 3] = 0.0
+    w[0, 3] = 1.0
+    w[D + 1, 3] = 2.0
+    h = np.zeros((1, H))
+    h[0, 3] = 1.0
+    g_q = np.linspace(-0.5, 0.75, D)
+    g_k = np.linspace(0.3, -0.6, D)
+    pt, ph, pw = 5, 9, 40
+    qi, ki, qf, kf = F.indexer_frontend(h, np.array([[pt], [ph], [pw]]), w, g_q, g_k, base, 20.0, 7.0, D,
+                                        prequant=True, mrope_sections=(1, 1, 2))
+    vq = 20.0 * (1 + g_q[0]) / np.sqrt(1.0 / D + F.RMS_EPS)
+    vk = 7.0 * 2.0 * (1 + g_k[1]) / np.sqrt(4.0 / D + F.RMS_EPS)
+    a = ph * base ** (-2.0 / D)
+    want_q = np.zeros(D)
+    want_q[0], want_q[D // 2] = vq * np.cos(pt), vq * np.sin(pt)
+    want_k = np.zeros(D)
+    want_k[1], want_k[1 + D // 2] = vk * np.cos(a), vk * np.sin(a)
+    assert np.allclose(qf[0], want_q, atol=1e-12) and np.allclose(kf[0], want_k, atol=1e-12)
+    assert qi[0].tolist() == np.clip(np.rint(want_q), -127, 127).astype(int).tolist()
+    assert ki[0].tolist() == np.clip(np.rint(want_k), -127, 127).astype(int).tolist()

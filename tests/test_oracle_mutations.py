@@ -10,6 +10,8 @@ import numpy as np
 import pytest
 
 from oracle import qsa_oracle as O
+import oracle.qsa_frontend_oracle as F
+import tests.test_oracle_frontend_pins as FP
 import tests.test_oracle_pins as P
 
 
@@ -215,3 +217,39 @@ def test_tail_of_the_selecting_row_instead_of_the_own_row_is_caught(monkeypatch)
     monkeypatch.setattr(O, "split_token_positions",
                         lambda blocks, sel_seq_len, row_seq_len, P_: orig(blocks, sel_seq_len, sel_seq_len, P_))
     assert _fails(P.test_rows_follow_row_sel_with_their_own_tails, "bf16")
+
+
+def _mrope_variant(assign):
+    """An MRoPE whose frequency -> component assignment is assign(i, sections)."""
+    def bad(x, pos3, base, sections):
+        D = x.shape[-1]
+        h = D // 2
+        comp = np.array([assign(i, sections) for i in range(h)])
+        pos3 = np.asarray(pos3, dtype=np.float64)
+        i = np.arange(h, dtype=np.float64)
+        ang = pos3[comp, :].T * base ** (-2.0 * i / D)[None, :]
+        c, s = np.cos(ang), np.sin(ang)
+        a, b = x[:, :h], x[:, h:]
+        return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+    return bad
+
+
+def _contig(i, sec):
+    return 0 if i < sec[0] else (1 if i < sec[0] + sec[1] else 2)
+
+
+def test_mrope_interleaved_sections_are_caught(monkeypatch):
+    monkeypatch.setattr(F, "mrope", _mrope_variant(lambda i, sec: i % 3))
+    assert _fails(FP.test_mrope_each_section_turns_with_its_own_component_only)
+    assert _fails(FP.test_mrope_first_pair_of_each_section_closed_form)
+
+
+def test_mrope_swapped_height_and_width_is_caught(monkeypatch):
+    monkeypatch.setattr(F, "mrope", _mrope_variant(lambda i, sec: [0, 2, 1][_contig(i, sec)]))
+    assert _fails(FP.test_mrope_each_section_turns_with_its_own_component_only)
+    assert _fails(FP.test_composed_front_end_with_mrope) or _fails(FP.test_mrope_first_pair_of_each_section_closed_form)
+
+
+def test_mrope_sections_off_by_one_are_caught(monkeypatch):
+    monkeypatch.setattr(F, "mrope", _mrope_variant(lambda i, sec: _contig(i + 1, sec) if i + 1 < sum(sec) else 2))
+    assert _fails(FP.test_mrope_each_section_turns_with_its_own_component_only)
