@@ -61,6 +61,8 @@ SIGNATURES = {
     "qsa_indexer_project_workspace_size": (ctypes.c_size_t, [_I, _I, _I]),
     "qsa_indexer_project": (_I, [_I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                  _P, _P, _P, ctypes.c_size_t, _P]),
+    "qsa_indexer_project_mrope": (_I, [_I, _I, _I, _P, _P, _I, _I, _I, _P, _P, _P, ctypes.c_float, ctypes.c_float,
+                                       ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
     "qsa_status_string": (ctypes.c_char_p, [_I]),
     "qsa_last_error": (ctypes.c_char_p, []),
     "qsa_version": (ctypes.c_char_p, []),

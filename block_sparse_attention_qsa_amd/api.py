@@ -246,22 +246,45 @@ def qsa_indexer_project_workspace_size(num_tokens: int, hidden_dim: int, index_d
     return int(_lib.load().qsa_indexer_project_workspace_size(num_tokens, hidden_dim, index_dim))
 
 
-def qsa_indexer_project(hidden: torch.Tensor, positions: torch.Tensor, w_qk: torch.Tensor, g_q: torch.Tensor,
-                        g_k: torch.Tensor, q_index: torch.Tensor, keys: torch.Tensor, rope_base: float = 10000.0,
-                        q_scale: float = 32.0, k_scale: float = 32.0, workspace: Optional[torch.Tensor] = None,
-                        stream=None) -> None:
-    """Indexer front end: hidden bf16 [T, H], w_qk bf16 [2D, H] -> q_index, keys int8 [T, D].
-    workspace: device scratch of qsa_indexer_project_workspace_size bytes (allocated here if None)."""
+def _project_args(hidden, positions, w_qk, g_q, g_k, q_index, keys, workspace, pos_shape):
     _dt(hidden, torch.bfloat16); _dt(w_qk, torch.bfloat16); _dt(positions, torch.int32)
     _dt(g_q, torch.float32); _dt(g_k, torch.float32); _dt(q_index, torch.int8); _dt(keys, torch.int8)
     T, H = hidden.shape
     D = q_index.shape[1]
     if w_qk.shape != (2 * D, H) or keys.shape != (T, D) or q_index.shape[0] != T:
         raise QSAError(_lib.QSA_ERR_INVALID_ARGUMENT, "shape mismatch between hidden, w_qk, q_index and keys")
+    if tuple(positions.shape) != pos_shape(T) or not positions.is_contiguous():
+        raise QSAError(_lib.QSA_ERR_INVALID_ARGUMENT, f"positions must be contiguous int32 {pos_shape(T)}")
     need = qsa_indexer_project_workspace_size(T, H, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=hidden.device)
+    return T, H, D, workspace
+
+
+def qsa_indexer_project(hidden: torch.Tensor, positions: torch.Tensor, w_qk: torch.Tensor, g_q: torch.Tensor,
+                        g_k: torch.Tensor, q_index: torch.Tensor, keys: torch.Tensor, rope_base: float = 10000.0,
+                        q_scale: float = 32.0, k_scale: float = 32.0, workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+    """Indexer front end: hidden bf16 [T, H], w_qk bf16 [2D, H] -> q_index, keys int8 [T, D].
+    workspace: device scratch of qsa_indexer_project_workspace_size bytes (allocated here if None)."""
+    T, H, D, workspace = _project_args(hidden, positions, w_qk, g_q, g_k, q_index, keys, workspace, lambda t: (t,))
     _check(_lib.load().qsa_indexer_project(T, H, D, _ptr(hidden), _ptr(positions), _ptr(w_qk), _ptr(g_q),
                                            _ptr(g_k), float(rope_base), float(q_scale), float(k_scale),
                                            _ptr(q_index), _ptr(keys), _ptr(workspace),
                                            workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def qsa_indexer_project_mrope(hidden: torch.Tensor, positions: torch.Tensor, sections, w_qk: torch.Tensor,
+                              g_q: torch.Tensor, g_k: torch.Tensor, q_index: torch.Tensor, keys: torch.Tensor,
+                              rope_base: float = 10000.0, q_scale: float = 32.0, k_scale: float = 32.0,
+                              workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """The front end with MRoPE: positions int32 [3, T] (temporal, height, width),
+    sections (s_t, s_h, s_w) summing to D/2."""
+    T, H, D, workspace = _project_args(hidden, positions, w_qk, g_q, g_k, q_index, keys, workspace,
+                                       lambda t: (3, t))
+    s_t, s_h, s_w = (int(v) for v in sections)
+    _check(_lib.load().qsa_indexer_project_mrope(T, H, D, _ptr(hidden), _ptr(positions), s_t, s_h, s_w,
+                                                 _ptr(w_qk), _ptr(g_q), _ptr(g_k), float(rope_base),
+                                                 float(q_scale), float(k_scale), _ptr(q_index), _ptr(keys),
+                                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                 _stream(stream)))

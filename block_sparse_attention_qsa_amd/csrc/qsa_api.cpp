@@ -371,32 +371,63 @@ size_t qsa_indexer_project_workspace_size(int32_t num_tokens, int32_t hidden_dim
   return qsa::indexer_project_workspace_bytes(num_tokens, hidden_dim, index_dim);
 }
 
+namespace {
+
+// Shared by the 1-D and MRoPE front-end calls; name is the caller's, for messages.
+qsa_status indexer_project_common(const char* name, int32_t num_tokens, int32_t hidden_dim, int32_t index_dim,
+                                  const void* hidden, const int32_t* positions, int32_t pos_stride, int32_t sec1,
+                                  int32_t sec2, const void* w_qk, const float* g_q, const float* g_k,
+                                  float rope_base, float q_scale, float k_scale, int8_t* q_index, int8_t* keys,
+                                  void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (num_tokens < 0 || num_tokens > (1 << 24))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: num_tokens must be in [0, 2^24] (got %d)", name, num_tokens);
+  if (hidden_dim < 32 || hidden_dim % 32 != 0 || hidden_dim > 65536)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: hidden_dim must be a multiple of 32 in [32, 65536] (got %d)", name,
+                hidden_dim);
+  if (index_dim != 32 && index_dim != 64 && index_dim != 128)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: index_dim %d not built (32, 64, 128)", name, index_dim);
+  if (!(rope_base > 1.0f) || !(q_scale > 0.0f) || !(k_scale > 0.0f) || !std::isfinite(rope_base) ||
+      !std::isfinite(q_scale) || !std::isfinite(k_scale))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: rope_base must be > 1 and the scales > 0, all finite", name);
+  if (num_tokens == 0) return QSA_OK;
+  if (!hidden || !positions || !w_qk || !g_q || !g_k || !q_index || !keys)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL array argument", name);
+  if (!aligned(hidden, 16) || !aligned(w_qk, 16) || !aligned(q_index, 4) || !aligned(keys, 4))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: hidden and w_qk need 16-byte, q_index and keys 4-byte alignment",
+                name);
+  if (!workspace || !aligned(workspace, 16))
+    return fail(QSA_ERR_WORKSPACE, "%s: workspace is NULL or not 16-byte aligned", name);
+  const size_t need = indexer_project_workspace_bytes(num_tokens, hidden_dim, index_dim);
+  if (ws_bytes < need) return fail(QSA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", name, ws_bytes, need);
+  return launch_indexer_project(num_tokens, hidden_dim, index_dim, hidden, positions, pos_stride, sec1, sec2, w_qk,
+                                g_q, g_k, rope_base, q_scale, k_scale, q_index, keys,
+                                reinterpret_cast<float*>(workspace), stream);
+}
+
+}  // namespace
+
 qsa_status qsa_indexer_project(int32_t num_tokens, int32_t hidden_dim, int32_t index_dim, const void* hidden,
                                const int32_t* positions, const void* w_qk, const float* g_q, const float* g_k,
                                float rope_base, float q_scale, float k_scale, int8_t* q_index, int8_t* keys,
                                void* workspace, size_t ws_bytes, hipStream_t stream) {
-  if (num_tokens < 0 || num_tokens > (1 << 24))
-    return fail(QSA_ERR_INVALID_ARGUMENT, "num_tokens must be in [0, 2^24] (got %d)", num_tokens);
-  if (hidden_dim < 32 || hidden_dim % 32 != 0 || hidden_dim > 65536)
-    return fail(QSA_ERR_INVALID_ARGUMENT, "hidden_dim must be a multiple of 32 in [32, 65536] (got %d)", hidden_dim);
-  if (index_dim != 32 && index_dim != 64 && index_dim != 128)
-    return fail(QSA_ERR_UNSUPPORTED, "index_dim %d not built (32, 64, 128)", index_dim);
-  if (!(rope_base > 1.0f) || !(q_scale > 0.0f) || !(k_scale > 0.0f) || !std::isfinite(rope_base) ||
-      !std::isfinite(q_scale) || !std::isfinite(k_scale))
-    return fail(QSA_ERR_INVALID_ARGUMENT, "rope_base must be > 1 and the scales > 0, all finite");
-  if (num_tokens == 0) return QSA_OK;
-  if (!hidden || !positions || !w_qk || !g_q || !g_k || !q_index || !keys)
-    return fail(QSA_ERR_INVALID_ARGUMENT, "qsa_indexer_project: NULL array argument");
-  if (!aligned(hidden, 16) || !aligned(w_qk, 16) || !aligned(q_index, 4) || !aligned(keys, 4))
+  return indexer_project_common("qsa_indexer_project", num_tokens, hidden_dim, index_dim, hidden, positions, 0,
+                                index_dim / 2, index_dim / 2, w_qk, g_q, g_k, rope_base, q_scale, k_scale, q_index,
+                                keys, workspace, ws_bytes, stream);
+}
+
+qsa_status qsa_indexer_project_mrope(int32_t num_tokens, int32_t hidden_dim, int32_t index_dim, const void* hidden,
+                                     const int32_t* positions, int32_t section_t, int32_t section_h,
+                                     int32_t section_w, const void* w_qk, const float* g_q, const float* g_k,
+                                     float rope_base, float q_scale, float k_scale, int8_t* q_index, int8_t* keys,
+                                     void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (section_t < 0 || section_h < 0 || section_w < 0 ||
+      (int64_t)section_t + section_h + section_w != index_dim / 2)
     return fail(QSA_ERR_INVALID_ARGUMENT,
-                "qsa_indexer_project: hidden and w_qk need 16-byte, q_index and keys 4-byte alignment");
-  if (!workspace || !aligned(workspace, 16))
-    return fail(QSA_ERR_WORKSPACE, "qsa_indexer_project: workspace is NULL or not 16-byte aligned");
-  const size_t need = indexer_project_workspace_bytes(num_tokens, hidden_dim, index_dim);
-  if (ws_bytes < need)
-    return fail(QSA_ERR_WORKSPACE, "qsa_indexer_project: workspace has %zu bytes, needs %zu", ws_bytes, need);
-  return launch_indexer_project(num_tokens, hidden_dim, index_dim, hidden, positions, w_qk, g_q, g_k, rope_base,
-                                q_scale, k_scale, q_index, keys, reinterpret_cast<float*>(workspace), stream);
+                "qsa_indexer_project_mrope: sections (%d, %d, %d) must be >= 0 and sum to index_dim / 2 = %d",
+                section_t, section_h, section_w, index_dim / 2);
+  return indexer_project_common("qsa_indexer_project_mrope", num_tokens, hidden_dim, index_dim, hidden, positions,
+                                num_tokens, section_t, section_t + section_h, w_qk, g_q, g_k, rope_base, q_scale,
+                                k_scale, q_index, keys, workspace, ws_bytes, stream);
 }
 
 const char* qsa_status_string(qsa_status s) {

@@ -2,12 +2,16 @@
 //
 // Method ("PR #53896 完整报告", key source snippets, QSAIndexer): the indexer
 // projects Q and K from the hidden states, normalises them with a Gemma-style
-// RMSNorm and applies a 1-D rotary embedding before the keys enter the raw-key
-// ring and the query selects.  Here, per token t at position p:
+// RMSNorm and applies a rotary embedding, 1-D or MRoPE, before the keys enter
+// the raw-key ring and the query selects.  Here, per token t at position p:
 //   [q | k] = h_t W^T            W bf16 [2D, H] (q rows, then k rows), fp32 sums
 //   x <- x / sqrt(mean(x^2) + 1e-6) * (1 + g)          (g_q for q, g_k for k)
 //   (x_i, x_{i+D/2}) rotated by p * base^(-2i/D)       (after the norm)
 //   int8 = clamp(round-half-even(x * scale), -127, 127)
+// With MRoPE p has three components (temporal, height, width: positions
+// [3, T]) and pair i takes the component of the contiguous section of the D/2
+// frequencies it lies in (sections [0, sec1), [sec1, sec2), [sec2, D/2)); the
+// 1-D call is the same kernel with one component (stride 0, sec1 = D/2).
 //
 // Two kernels.  project (grid: 64-token block x slice of H): each of the 4
 // waves owns a quarter of the output columns for all 64 tokens (four MFMA
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(kFeThreads) void project_kernel(
 template <int D>
 __global__ __launch_bounds__(kFeThreads) void finish_kernel(
     int32_t T, int32_t nslices, const float* __restrict__ part, int32_t t_pad, const int32_t* __restrict__ positions,
-    const float* __restrict__ g_q, const float* __restrict__ g_k, float base, float q_scale, float k_scale,
+    int32_t pos_stride, int32_t sec1, int32_t sec2, const float* __restrict__ g_q, const float* __restrict__ g_k, float base, float q_scale, float k_scale,
     int8_t* __restrict__ q_out, int8_t* __restrict__ k_out) {
   constexpr int kPer = D / 8;  // dims per thread
   __shared__ double inv_freq[D / 2];
@@ -145,7 +149,10 @@ __global__ __launch_bounds__(kFeThreads) void finish_kernel(
   for (int e = 0; e < kPer; ++e) x[e] = x[e] * inv * (1.0f + g[part_i * kPer + e]);
   __syncthreads();  // inv_freq
   // rotation: dims i < D/2 live in parts 0..3, their partners i + D/2 in parts 4..7
-  const double pos = (double)positions[tokc];
+  // the token's three position components (one, read three times, for 1-D)
+  const double pos0 = (double)positions[tokc];
+  const double pos1 = (double)positions[(size_t)pos_stride + tokc];
+  const double pos2 = (double)positions[2 * (size_t)pos_stride + tokc];
   const float sc = isk ? k_scale : q_scale;
   uint32_t packed[kPer / 4];
 #pragma unroll
@@ -154,6 +161,7 @@ __global__ __launch_bounds__(kFeThreads) void finish_kernel(
     const int i = (part_i & 3) * kPer + e;  // pair index < D/2
     // angle reduced to [-pi, pi] in double (exact enough for positions up to
     // 2^23), then the single-precision sine and cosine of the remainder
+    const double pos = (i < sec1) ? pos0 : (i < sec2 ? pos1 : pos2);
     const double ang = pos * inv_freq[i];
     const double r = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
     float s, c;
@@ -196,7 +204,7 @@ size_t indexer_project_workspace_bytes(int32_t T, int32_t H, int32_t D) {
 }
 
 qsa_status launch_indexer_project(int32_t T, int32_t H, int32_t D, const void* hidden, const int32_t* positions,
-                                  const void* w_qk, const float* g_q, const float* g_k, float base, float q_scale,
+                                  int32_t pos_stride, int32_t sec1, int32_t sec2, const void* w_qk, const float* g_q, const float* g_k, float base, float q_scale,
                                   float k_scale, int8_t* q_index, int8_t* keys, float* ws, hipStream_t stream) {
   if (T == 0) return QSA_OK;
   int32_t ns, sl, tp;
@@ -211,7 +219,7 @@ qsa_status launch_indexer_project(int32_t T, int32_t H, int32_t D, const void* h
       hipLaunchKernelGGL(project_kernel<DD>, pgrid, dim3(kFeThreads), 0, stream, T, H, sl, h, w, ws, tp);   \
       if (check_launch("qsa_indexer_project(project)") != QSA_OK) return QSA_ERR_HIP;                       \
       hipLaunchKernelGGL(finish_kernel<DD>, fgrid, dim3(kFeThreads), 0, stream, T, ns, ws, tp, positions,   \
-                         g_q, g_k, base, q_scale, k_scale, q_index, keys);                                   \
+                         pos_stride, sec1, sec2, g_q, g_k, base, q_scale, k_scale, q_index, keys);           \
       break;
     QSA_FE_CASE(32)
     QSA_FE_CASE(64)

@@ -71,8 +71,10 @@ qsa_status launch_index_topk_noalloc(const qsa_config& c, int32_t S, int32_t max
 
 size_t indexer_project_workspace_bytes(int32_t T, int32_t H, int32_t D);
 
+// positions: [T] (pos_stride 0, sec1 = sec2 = D/2) or MRoPE [3, T] (pos_stride T,
+// frequency sections [0, sec1), [sec1, sec2), [sec2, D/2))
 qsa_status launch_indexer_project(int32_t T, int32_t H, int32_t D, const void* hidden, const int32_t* positions,
-                                  const void* w_qk, const float* g_q, const float* g_k, float base, float q_scale,
+                                  int32_t pos_stride, int32_t sec1, int32_t sec2, const void* w_qk, const float* g_q, const float* g_k, float base, float q_scale,
                                   float k_scale, int8_t* q_index, int8_t* keys, float* ws, hipStream_t stream);
 
 qsa_status launch_sparse_decode(const qsa_config& c, int32_t R, int32_t S, int32_t qps, int32_t P,

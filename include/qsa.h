@@ -390,6 +390,28 @@ qsa_status qsa_indexer_project(int32_t num_tokens, int32_t hidden_dim, int32_t i
                                float rope_base, float q_scale, float k_scale, int8_t* q_index, int8_t* keys,
                                void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * qsa_indexer_project_mrope -- qsa_indexer_project with the multimodal rotary
+ * embedding.  [PR53896] (key source snippets, QSAIndexer): the AMD indexer
+ * combines the Gemma RMSNorm with a 1-D or an MRoPE rotation, and its forward
+ * takes positions with a leading component axis (positions[..., :num_tokens]).
+ * Here positions is int32 [3, T]: the temporal, height and width components of
+ * every token (row c, column t).  The D/2 rotation frequencies are split into
+ * three contiguous sections of section_t, section_h and section_w frequencies;
+ * pair (x_i, x_{i+D/2}) turns by p_c[t] * rope_base^(-2i/D) with c the section
+ * of i (0 for i < section_t, 1 for i < section_t + section_h, else 2).  A
+ * token whose three components are equal (text) gets exactly what
+ * qsa_indexer_project gives at that position.  Everything else, the
+ * workspace included, as qsa_indexer_project.
+ *   section_t, section_h, section_w >= 0 with sum index_dim / 2.
+ * Errors: INVALID_ARGUMENT (also for the sections), UNSUPPORTED, WORKSPACE, HIP.
+ */
+qsa_status qsa_indexer_project_mrope(int32_t num_tokens, int32_t hidden_dim, int32_t index_dim, const void* hidden,
+                                     const int32_t* positions, int32_t section_t, int32_t section_h,
+                                     int32_t section_w, const void* w_qk, const float* g_q, const float* g_k,
+                                     float rope_base, float q_scale, float k_scale, int8_t* q_index, int8_t* keys,
+                                     void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Human-readable name of a status. */
 const char* qsa_status_string(qsa_status status);
 

@@ -244,6 +244,22 @@ def test_indexer_project_rejects(lib):
     assert fe(T=0) == 0
 
 
+def test_indexer_project_mrope_rejects(lib):
+    n = lib.qsa_indexer_project_workspace_size(8, 256, 64)
+
+    def fe(T=8, D=64, sec=(8, 12, 12), ws=FAKE, nbytes=n, base=10000.0):
+        return lib.qsa_indexer_project_mrope(T, 256, D, FAKE, FAKE, sec[0], sec[1], sec[2], FAKE, FAKE, FAKE, base,
+                                             32.0, 32.0, FAKE, FAKE, ws, nbytes, None)
+    assert fe(sec=(8, 12, 11)) == 1       # sections must sum to D/2
+    assert fe(sec=(-1, 17, 16)) == 1
+    assert fe(D=128) == 1                 # 8 + 12 + 12 != 64
+    assert fe(D=128, sec=(16, 24, 24), nbytes=n) == 3    # a D=128 workspace is larger
+    assert fe(ws=None) == 3
+    assert fe(base=0.5) == 1
+    assert fe(T=-1) == 1
+    assert fe(T=0) == 0
+
+
 
 def test_compress_index_topk_rejects(lib):
     c = cfg()

@@ -1,4 +1,5 @@
-"""GPU parity of the indexer front end (qsa_indexer_project) against the
+"""GPU parity of the indexer front end (qsa_indexer_project, and
+qsa_indexer_project_mrope with three position components) against the
 front-end oracle, and of the chain front end -> compress -> selection.
 
 The int8 outputs must equal the oracle's, except by one where the oracle's
@@ -109,3 +110,58 @@ def test_front_end_feeds_compress_and_selection():
                 f"seed {seed} request {b}"
         compared += 1
     assert compared >= 1, "every seed hit a rounding boundary"
+
+
+def _pos3(T, seed, max_pos=1 << 23):
+    """Three position components per token: independent random components, and
+    for about 30 % of the tokens three equal ones (text); extremes included."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    p = torch.randint(0, max_pos, (3, T), generator=g, dtype=torch.int32)
+    text = torch.rand(T, generator=g) < 0.3
+    p[1][text] = p[0][text]
+    p[2][text] = p[0][text]
+    if T >= 3:
+        p[:, 0] = torch.tensor([0, 0, 0], dtype=torch.int32)
+        p[:, 1] = torch.tensor([5, max_pos - 1, 0], dtype=torch.int32)
+        p[:, 2] = torch.tensor([max_pos - 1, 7, max_pos - 1], dtype=torch.int32)
+    return p.contiguous()
+
+
+@pytest.mark.parametrize("T,H,D,sec", [(1, 64, 64, (8, 12, 12)), (37, 1024, 128, (16, 24, 24)),
+                                       (300, 4096, 64, (32, 0, 0)), (64, 512, 32, (0, 8, 8))])
+def test_indexer_project_mrope_matches_oracle(T, H, D, sec):
+    base, qs, ks = 10000.0, 32.0, 24.0
+    hidden, w, gq, gk, _ = inputs(T, H, D, seed=T * 5 + H + D)
+    pos3 = _pos3(T, seed=T + D)
+    say(f"[gpu] indexer front end (MRoPE {sec}) T={T} H={H} D={D}")
+    q = torch.full((T, D), 99, dtype=torch.int8, device=DEV)
+    k = torch.full((T, D), 99, dtype=torch.int8, device=DEV)
+    api.qsa_indexer_project_mrope(hidden.to(DEV), pos3.to(DEV), sec, w.to(DEV), gq.to(DEV), gk.to(DEV), q, k,
+                                  rope_base=base, q_scale=qs, k_scale=ks)
+    torch.cuda.synchronize()
+    h = F.bf16_bits_to_f64(hidden.view(torch.int16).numpy())
+    wf = F.bf16_bits_to_f64(w.view(torch.int16).numpy())
+    rq, rk, pq, pk = F.indexer_frontend(h, pos3.numpy(), wf, gq.numpy().astype(np.float64),
+                                        gk.numpy().astype(np.float64), base, qs, ks, D, prequant=True,
+                                        mrope_sections=sec)
+    nq = check_int8(q.cpu().numpy(), rq, pq, "q")
+    nk = check_int8(k.cpu().numpy(), rk, pk, "k")
+    say(f"[gpu]   boundary differences q {nq}, k {nk}")
+
+
+def test_mrope_with_equal_components_is_the_1d_call_bit_for_bit():
+    T, H, D = 129, 1024, 64
+    hidden, w, gq, gk, pos = inputs(T, H, D, seed=77)
+    pos3 = torch.stack([pos, pos, pos]).contiguous()
+    outs = []
+    for mrope in (False, True):
+        q = torch.full((T, D), 99, dtype=torch.int8, device=DEV)
+        k = torch.full((T, D), 99, dtype=torch.int8, device=DEV)
+        if mrope:
+            api.qsa_indexer_project_mrope(hidden.to(DEV), pos3.to(DEV), (8, 12, 12), w.to(DEV), gq.to(DEV),
+                                          gk.to(DEV), q, k)
+        else:
+            api.qsa_indexer_project(hidden.to(DEV), pos.to(DEV), w.to(DEV), gq.to(DEV), gk.to(DEV), q, k)
+        torch.cuda.synchronize()
+        outs.append((q.cpu(), k.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
