@@ -20,6 +20,7 @@ QSA_ERR_HIP = 4
 QSA_KV_BF16 = 0
 QSA_KV_FP8_E4M3 = 1
 QSA_MAX_SEQ_LEN = 4 * (1 << 21)
+QSA_RING_SIZE = 8
 QSA_OUT_F32 = 0
 QSA_OUT_BF16 = 1
 
@@ -34,6 +35,7 @@ class qsa_config(ctypes.Structure):
         ("topk_blocks", ctypes.c_int32),
         ("page_size", ctypes.c_int32),
         ("max_pages_per_req", ctypes.c_int32),
+        ("ring_size", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
     ]

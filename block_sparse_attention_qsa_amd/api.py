@@ -42,13 +42,14 @@ class QSAConfig:
     kv_dtype: str = "bf16"  # "bf16" | "fp8"
     softmax_scale: float = 0.0  # 0 => 1/sqrt(head_dim)
     compress_ratio: int = 4
+    ring_size: int = _lib.QSA_RING_SIZE
 
     def to_c(self) -> _lib.qsa_config:
         scale = self.softmax_scale if self.softmax_scale > 0 else self.head_dim ** -0.5
         dt = {"bf16": _lib.QSA_KV_BF16, "fp8": _lib.QSA_KV_FP8_E4M3}.get(self.kv_dtype, -1)
         return _lib.qsa_config(self.num_q_heads, self.num_kv_heads, self.head_dim, self.index_dim,
                                self.compress_ratio, self.topk_blocks, self.page_size,
-                               self.max_pages_per_req, dt, scale)
+                               self.max_pages_per_req, self.ring_size, dt, scale)
 
 
 def _check(st: int) -> None:

@@ -36,6 +36,8 @@ static qsa_status check_config(const qsa_config* c, bool need_index, bool need_a
   if (!c) return fail(QSA_ERR_INVALID_ARGUMENT, "cfg is NULL");
   if (c->compress_ratio != 4)
     return fail(QSA_ERR_INVALID_ARGUMENT, "compress_ratio must be 4 (got %d)", c->compress_ratio);
+  if (c->ring_size != QSA_RING_SIZE)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "ring_size must be %d (got %d)", QSA_RING_SIZE, c->ring_size);
   if (c->page_size < 16 || !is_pow2(c->page_size) || c->page_size % c->compress_ratio)
     return fail(QSA_ERR_INVALID_ARGUMENT,
                 "page_size must be a power of two >= 16 divisible by the compress ratio (got %d)",

@@ -90,9 +90,15 @@ typedef struct {
   int32_t page_size;         /* tokens per page: power of two, >= 16 ([PR53896]:
                                 the ratio must divide the block size)             */
   int32_t max_pages_per_req; /* row stride of block_table                         */
+  int32_t ring_size;         /* slots of the raw-key ring per request: must be 8
+                                (QSA_RING_SIZE; [PR53896]: the indexer keeps the
+                                latest token keys in a ring before pooling)       */
   int32_t kv_dtype;          /* qsa_kv_dtype                                       */
   float softmax_scale;       /* logits are scale * q.k (1/sqrt(d) usually)         */
 } qsa_config;
+
+/* Raw-key ring slots per request (qsa_config.ring_size): the last 8 tokens. */
+#define QSA_RING_SIZE 8
 
 /* Largest context one row may have: 2^21 micro-blocks (8,388,608 tokens). */
 #define QSA_MAX_SEQ_LEN (4 * (1 << 21))

@@ -22,7 +22,7 @@ def declared_functions():
 
 def cfg(**kw):
     base = dict(num_q_heads=16, num_kv_heads=2, head_dim=128, index_dim=64, compress_ratio=4,
-                topk_blocks=512, page_size=64, max_pages_per_req=4096, kv_dtype=0, softmax_scale=0.088)
+                topk_blocks=512, page_size=64, max_pages_per_req=4096, ring_size=8, kv_dtype=0, softmax_scale=0.088)
     base.update(kw)
     return _lib.qsa_config(**base)
 
@@ -61,6 +61,7 @@ def compress(lib, c, nreq=1, **kw):
     (dict(compress_ratio=3), 1), (dict(compress_ratio=8), 1), (dict(page_size=48), 1),
     (dict(page_size=8), 1), (dict(topk_blocks=0), 1), (dict(topk_blocks=4096), 1),
     (dict(max_pages_per_req=0), 1), (dict(index_dim=48), 2), (dict(index_dim=0), 1),
+    (dict(ring_size=4), 1), (dict(ring_size=0), 1), (dict(ring_size=16), 1),
 ])
 def test_compress_rejects_bad_config(lib, bad, code):
     assert compress(lib, cfg(**bad)) == code
