@@ -471,6 +471,7 @@ struct RowLds {
   __align__(16) uint32_t rhist[kRadixPasses][256];
   uint64_t cand[kCandLds];
   uint64_t bm[kWordsLds];  // the row's selection (rows of up to kWordsLds * 64 blocks)
+  uint32_t slot_sums[2][kFinThreads / 64];  // emission: per word slot, per wave
   int32_t T;
   uint32_t above, n, nfb;
   uint16_t fb[kMaxChunksPerRow];  // chunks read again from their scores
@@ -742,13 +743,15 @@ struct RowSelector {
     if (nb == 0) return;
     const int per = (nwords + kFinThreads - 1) / kFinThreads;  // <= kWordsLds / kFinThreads
     if (per <= 2) emit_words<2>(per, i0, i1, list, each);
-    else emit_words<kWordsLds / kFinThreads>(per, i0, i1, list, each);
+    else emit_words_contiguous<kWordsLds / kFinThreads>(per, i0, i1, list, each);
   }
 
-  // emit_run with up to N bitmap words per thread, held in registers (read
-  // once for the popcounts; the walk then runs from registers).
+  // Rows of more than 1,024 words (over 256k tokens): each thread owns `per`
+  // consecutive words (one block scan of the per-thread counts); with N slots
+  // per thread the interleaved layout below would take N wave scans, which
+  // cost more there than the walk it spreads.
   template <int N, class Each>
-  __device__ __forceinline__ void emit_words(int per, int i0, int i1, int32_t* list, Each&& each) {
+  __device__ __forceinline__ void emit_words_contiguous(int per, int i0, int i1, int32_t* list, Each&& each) {
     const int tid = threadIdx.x;
     const int w0 = min(nwords, tid * per), nw = min(nwords, w0 + per) - w0;
     uint64_t wv[N];
@@ -776,6 +779,58 @@ struct RowSelector {
           }
         } else {
           pos += c;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // emit_run for rows of up to N * 512 words, held in registers (read once
+  // for the popcounts; the walk then runs from registers).  Word w is
+  // thread w mod 512's slot w / 512: consecutive words sit in consecutive
+  // threads, so the words of a run spread over many threads and waves instead
+  // of being walked one after another by a few threads of one wave.  A word's
+  // rank is the total of the slots before its own plus the prefix of its slot
+  // over the threads before it (one wave scan per slot, one barrier).
+  template <int N, class Each>
+  __device__ __forceinline__ void emit_words(int per, int i0, int i1, int32_t* list, Each&& each) {
+    static_assert(N <= 2, "slot_sums holds two slots");
+    (void)per;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    uint64_t wv[N];
+    uint32_t c[N], inc[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const int w = k * kFinThreads + tid;
+      wv[k] = (w < nwords) ? L.bm[min(w, kWordsLds - 1)] : 0ull;
+      c[k] = (uint32_t)__popcll(wv[k]);
+      inc[k] = wave_incl_scan(c[k]);
+      if (lane_id() == 63) L.slot_sums[k][wave] = inc[k];
+    }
+    __syncthreads();
+    uint32_t base = 0;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      uint32_t before = 0, tot = 0;
+#pragma unroll
+      for (int x = 0; x < kFinThreads / 64; ++x) {
+        const uint32_t v = L.slot_sums[k][x];
+        tot += v;
+        before += (x < wave) ? v : 0u;
+      }
+      uint32_t pos = base + before + inc[k] - c[k];
+      base += tot;
+      if ((int)pos < i1 && (int)(pos + c[k]) > i0) {  // this word holds part of the run
+        uint64_t m = wv[k];
+        const int w = k * kFinThreads + tid;
+        while (m) {
+          const int bit = __ffsll((long long)m) - 1;
+          m &= m - 1;
+          if ((int)pos >= i0 && (int)pos < i1) {
+            list[pos - i0] = w * 64 + bit;
+            each((int)pos - i0, w * 64 + bit);
+          }
+          ++pos;
         }
       }
     }
