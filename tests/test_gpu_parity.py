@@ -345,3 +345,34 @@ def test_graph_replay_matches_eager():
             assert torch.equal(a, b), f"replay {i}"
         layer.step()  # eager work between replays
         torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ merge at scale
+
+@pytest.mark.parametrize("P,R,H,d", [(5, 300, 16, 128), (4, 2048, 16, 64), (3, 7, 16, 128)])
+def test_merge_matches_oracle_small_and_many_pairs(P, R, H, d):
+    """Random partials (with empty splits and rows whose splits are all empty)
+    merged on the GPU against the oracle's merge; the first two shapes have
+    4,800 and 32,768 (row, head) pairs (8 waves per workgroup), the last one
+    112 (one wave per workgroup).  fp32 and bf16 outputs."""
+    g = torch.Generator(device="cpu").manual_seed(P * 1000 + R + d)
+    o = torch.randn((P, R, H, d), generator=g)
+    l = torch.randn((P, R, H), generator=g) * 4.0
+    l[torch.rand((P, R, H), generator=g) < 0.3] = -math.inf   # empty splits
+    l[:, 1] = -math.inf                                       # a row with nothing at all
+    o[torch.isinf(l)] = 0.0
+    say(f"[gpu] merge P={P} R={R} H={H} d={d}")
+    ref_o, ref_l = O.merge_partials(o.numpy(), l.numpy())
+    od, ld = o.to(DEV), l.to(DEV)
+    outs = {}
+    for dt in (torch.float32, torch.bfloat16):
+        out = torch.full((R, H, d), 7.0, dtype=dt, device=DEV)
+        lse = torch.full((R, H), 7.0, dtype=torch.float32, device=DEV)
+        api.qsa_merge_partials(od, ld, out, lse)
+        torch.cuda.synchronize()
+        check_lse(lse.cpu().numpy(), ref_l, f"merge {dt}")
+        assert torch.isneginf(lse[1]).all() and (out[1].float() == 0).all()
+        outs[dt] = out
+    check_out(outs[torch.float32].cpu().numpy(), ref_o, 1e-5, "merge fp32")
+    # bf16 output: the fp32 merge rounded to nearest even (torch's cast)
+    assert torch.equal(outs[torch.bfloat16], outs[torch.float32].to(torch.bfloat16))
