@@ -20,8 +20,8 @@
 //            writes the chunk's candidate list (every block at or above the
 //            bin of its m-th best block; see chunk_candidates).
 //   finalize (select_row in qsa_select.h: one workgroup per selecting row
-//            here; qsa_select_sparse_decode runs it inside its attention
-//            kernel instead): the row's threshold bin T
+//            here; qsa_select_sparse_decode runs the same steps inside its
+//            attention kernel instead): the row's threshold bin T
 //            (fewer than k scores above T, at least k at or above it) from the
 //            row histogram; the chunks' lists, loaded in one round, are
 //            classified against T (a chunk whose list may be short is re-read
@@ -367,8 +367,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     const int32_t* __restrict__ sel_seq_len, int32_t k, int32_t max_seq_len,
     int32_t* __restrict__ topk, WsPtrs ws) {
   const int s = blockIdx.x;
-  const uint32_t t = ws.gen[0];
-  select_row<kBmLds, false>(s, sel_seq_len, k, max_seq_len, topk + (size_t)s * k, nullptr, ws, t, [] {});
+  const uint32_t t = select_row<kBmLds>(s, sel_seq_len, k, max_seq_len, topk + (size_t)s * k, ws);
   // Last, so that no store is outstanding while the phases above wait for
   // their loads (the wait counter covers stores too).
   clear_next_hist(ws, s, t);

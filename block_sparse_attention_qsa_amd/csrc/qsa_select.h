@@ -8,10 +8,11 @@
 //
 // The scan kernels (qsa_index.hip) leave per row: the exact int32 scores, a
 // histogram of the scores' top bits and, per chunk of 1,024 blocks, a candidate
-// list.  select_row turns that into the row's ascending top-k.  It runs in
-// the finalize kernel (one workgroup per row) and, inlined, at the head of the
-// fused selection + attention kernel (qsa_decode.hip), where every workgroup
-// of a row computes the same selection into its LDS.
+// list.  select_row turns that into the row's ascending top-k in the
+// finalize kernel (one workgroup per row); RowSelector below runs the same
+// steps at the head of the fused selection + attention kernel (qsa_decode.hip),
+// where every workgroup of a row computes the selection into its LDS and
+// lists only its own split's run.
 #pragma once
 
 #include "qsa_device.h"
@@ -158,23 +159,17 @@ constexpr int kRadixPasses = (32 + kBinShift + 7) / 8;  // 8-bit digits below th
 // from the workspace's row stride), so no mark or read of it branches on where
 // it lives.
 //
-// t: the workspace's count of scored calls (gen[0]); the scan left the row's
-// histogram in histogram t & 1.  Both rows are loaded (the count arrives with
-// them) and one is used; neither is written.  The caller clears the other
-// histogram for the next scan (clear_next_hist) and publishes t as selected.
+// Returns t, the workspace's count of scored calls (gen[0]): the scan left
+// the row's histogram in histogram t & 1.  Both rows are loaded (the count, a
+// vector load behind them, picks one: no dependent round trip); neither is
+// written.  The caller clears the other histogram for the next scan
+// (clear_next_hist) and publishes t as selected.
 //
-// kFused = false (finalize kernel, one workgroup per row): the result goes to
-// out (global, k entries); candidates beyond kCandLds spill to the workspace.
-// kFused = true (every workgroup of the fused kernel that serves row s): the
-// result goes to sel (LDS, k entries) and, when out is not null, to out too;
-// nothing is written to the workspace.  More than kCandLds threshold
-// candidates (rows of massively tied scores) are not stored: the radix select
-// and the marking then visit them again in the chunk lists and scores.
-// hook() runs once the first round of loads is in flight.
-template <bool kBmLds, bool kFused, class Hook>
-__device__ __forceinline__ void select_row(int s, const int32_t* __restrict__ sel_seq_len, int32_t k,
-                                           int32_t max_seq_len, int32_t* __restrict__ out, int32_t* sel,
-                                           const WsPtrs& ws, uint32_t t, Hook&& hook) {
+// One workgroup per row (the finalize kernel): the result goes to out (k
+// entries); threshold candidates beyond kCandLds spill to the workspace.
+template <bool kBmLds>
+__device__ __forceinline__ uint32_t select_row(int s, const int32_t* __restrict__ sel_seq_len, int32_t k,
+                                               int32_t max_seq_len, int32_t* __restrict__ out, const WsPtrs& ws) {
   constexpr int kPer = kBins / kFinThreads;
   __shared__ uint32_t sh[kFinThreads / 64];
   __shared__ __align__(16) uint32_t rhist[kRadixPasses][256];
@@ -201,31 +196,27 @@ __device__ __forceinline__ void select_row(int s, const int32_t* __restrict__ se
   uint32_t h0[kPer], h1[kPer];
   load_hist_desc<kFinThreads>(ghist0, h0);
   load_hist_desc<kFinThreads>(ghist0 + ws.hist_stride, h1);
+  const int32_t Lv = vload_same(sel_seq_len + s);
+  const int32_t tv = vload_same(reinterpret_cast<const int32_t*>(ws.gen));
   int cc = min(tid / tpc, nchunks_max - 1);
   uint32_t ci = cinfo[cc];
   uint64_t kk[kFinKeys];
 #pragma unroll
   for (int e = 0; e < kFinKeys; ++e) kk[e] = ckeys[(size_t)cc * kScoreChunk + sub * kFinKeys + e];
-  const int Lr = sel_seq_len[s];
-  hook();
-  // the histogram and the length before the length test below (the keys and
-  // cinfo, loaded after the histogram, are waited for only after the threshold)
-  asm volatile("" ::"s"(Lr));
+  asm volatile("" ::: "memory");  // the loads go out here, not sunk to where they are used
+  // the histogram, the length and the count before the length test below (the
+  // keys and cinfo, loaded after them, are waited for only after the threshold)
+  const int Lr = __builtin_amdgcn_readfirstlane(Lv);
+  const uint32_t t = (uint32_t)__builtin_amdgcn_readfirstlane(tv);
   uint32_t hc[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    asm volatile("" ::"v"(h0[i]), "v"(h1[i]));
-    hc[i] = (t & 1u) ? h1[i] : h0[i];
-  }
+  for (int i = 0; i < kPer; ++i) hc[i] = (t & 1u) ? h1[i] : h0[i];
 
   const int L = min(Lr, max_seq_len);
   const int nb = max(L, 0) >> 2;
   if (nb == 0) {  // nothing was scored: the histogram is untouched
-    for (int i = tid; i < k; i += kFinThreads) {
-      if (kFused) sel[i] = -1;
-      if (out) out[i] = -1;
-    }
-    return;
+    for (int i = tid; i < k; i += kFinThreads) out[i] = -1;
+    return t;
   }
   const uint32_t ks = (uint32_t)min(k, nb);
   const int nchunks = (nb + kScoreChunk - 1) / kScoreChunk;
@@ -252,7 +243,7 @@ __device__ __forceinline__ void select_row(int s, const int32_t* __restrict__ se
   };
   auto keep = [&](uint32_t i, uint64_t key) {
     if (i < (uint32_t)kCandLds) cand[i] = key;
-    else if (!kFused) gkeys[i] = key;
+    else gkeys[i] = key;
   };
   auto classify = [&](uint64_t key) {
     const int bin = score_bin(key_score(key));
@@ -355,78 +346,32 @@ __device__ __forceinline__ void select_row(int s, const int32_t* __restrict__ se
   // barrier per pass suffices: after it every wave reads the same counts and
   // finds the digit by itself.
   constexpr uint64_t kBinMask = ~((1ull << (32 + kBinShift)) - 1ull);
-  if (!kFused || n <= (uint32_t)kCandLds) {
-    const uint64_t mine = key_at(min((uint32_t)tid, n - 1));
-    uint64_t prefix = 0, mask = 0;  // (mask 0 keeps every candidate)
-    if (need < n) {
-      mask = kBinMask;
-      prefix = cand[0] & kBinMask;
-      uint32_t rem = need;
-      for (int p = 0, shift = 32 + kBinShift - 8;; ++p, shift = max(shift - 8, 0)) {
-        uint32_t* h = rhist[p];
-        if ((uint32_t)tid < n && (mine & mask) == prefix) atomicAdd(&h[(mine >> shift) & 0xff], 1u);
-        for (uint32_t i = tid + kFinThreads; i < n; i += kFinThreads) {
-          const uint64_t key = key_at(i);
-          if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 0xff], 1u);
-        }
-        __syncthreads();
-        uint32_t dsel, larger, cnt;
-        radix_digit(h, rem, dsel, larger, cnt);
-        rem -= larger;
-        prefix = (prefix & ~(0xffull << shift)) | ((uint64_t)dsel << shift);
-        mask |= 0xffull << shift;
-        if (cnt == rem || shift == 0) break;  // every remaining candidate with this prefix is kept
-      }
-    }
-    if ((uint32_t)tid < n && (mine & mask) >= prefix) mark(0xffffffffu - (uint32_t)(mine & 0xffffffffull));
-    for (uint32_t i = tid + kFinThreads; i < n; i += kFinThreads) {
-      const uint64_t key = key_at(i);
-      if ((key & mask) >= prefix) mark(0xffffffffu - (uint32_t)(key & 0xffffffffull));
-    }
-  } else {
-    // Fused, more candidates than the LDS holds (need <= k < n): every pass
-    // and the marking visit the threshold candidates where the classification
-    // found them, the chunk lists (local bin <= T) and the chunk scores (local
-    // bin above T), with the classification's thread-to-chunk mapping.
-    auto visit = [&](auto&& f) {
-      for (int c0 = 0; c0 < nchunks; c0 += cpr) {
-        const int c = c0 + tid / tpc;
-        if (c >= nchunks) continue;
-        const uint32_t cinf = cinfo[c];
-        if ((int)(cinf & 0xffffu) <= T) {
-          const uint32_t cnt = cinf >> 16;
-          for (uint32_t i = sub; i < cnt; i += tpc) {
-            const uint64_t key = ckeys[(size_t)c * kScoreChunk + i];
-            if (score_bin(key_score(key)) == T) f(key);
-          }
-        } else {
-          const int jn = min(kScoreChunk, nb - c * kScoreChunk);
-          for (int i = sub; i < jn; i += tpc) {
-            const uint32_t j = (uint32_t)(c * kScoreChunk + i);
-            const uint64_t key = cand_key(srow[j], j);
-            if (score_bin(key_score(key)) == T) f(key);
-          }
-        }
-      }
-    };
-    uint64_t mask = kBinMask, prefix = cand[0] & kBinMask;
+  const uint64_t mine = key_at(min((uint32_t)tid, n - 1));
+  uint64_t prefix = 0, mask = 0;  // (mask 0 keeps every candidate)
+  if (need < n) {
+    mask = kBinMask;
+    prefix = cand[0] & kBinMask;
     uint32_t rem = need;
     for (int p = 0, shift = 32 + kBinShift - 8;; ++p, shift = max(shift - 8, 0)) {
       uint32_t* h = rhist[p];
-      visit([&](uint64_t key) {
+      if ((uint32_t)tid < n && (mine & mask) == prefix) atomicAdd(&h[(mine >> shift) & 0xff], 1u);
+      for (uint32_t i = tid + kFinThreads; i < n; i += kFinThreads) {
+        const uint64_t key = key_at(i);
         if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 0xff], 1u);
-      });
+      }
       __syncthreads();
       uint32_t dsel, larger, cnt;
       radix_digit(h, rem, dsel, larger, cnt);
       rem -= larger;
       prefix = (prefix & ~(0xffull << shift)) | ((uint64_t)dsel << shift);
       mask |= 0xffull << shift;
-      if (cnt == rem || shift == 0) break;
+      if (cnt == rem || shift == 0) break;  // every remaining candidate with this prefix is kept
     }
-    visit([&](uint64_t key) {
-      if ((key & mask) >= prefix) mark(0xffffffffu - (uint32_t)(key & 0xffffffffull));
-    });
+  }
+  if ((uint32_t)tid < n && (mine & mask) >= prefix) mark(0xffffffffu - (uint32_t)(mine & 0xffffffffull));
+  for (uint32_t i = tid + kFinThreads; i < n; i += kFinThreads) {
+    const uint64_t key = key_at(i);
+    if ((key & mask) >= prefix) mark(0xffffffffu - (uint32_t)(key & 0xffffffffull));
   }
   __syncthreads();
 
@@ -441,17 +386,12 @@ __device__ __forceinline__ void select_row(int s, const int32_t* __restrict__ se
     while (m) {
       const int bit = __ffsll((long long)m) - 1;
       m &= m - 1;
-      if (pos < (uint32_t)k) {
-        if (kFused) sel[pos] = i * 64 + bit;
-        if (out) out[pos] = i * 64 + bit;
-      }
+      if (pos < (uint32_t)k) out[pos] = i * 64 + bit;
       ++pos;
     }
   }
-  for (int i = (int)ks + tid; i < k; i += kFinThreads) {
-    if (kFused) sel[i] = -1;
-    if (out) out[i] = -1;
-  }
+  for (int i = (int)ks + tid; i < k; i += kFinThreads) out[i] = -1;
+  return t;
 }
 
 // ---------------------------------------------------------------------------
