@@ -627,7 +627,18 @@ __global__ __launch_bounds__(kFinThreads) void select_decode_kernel(DecodeArgs a
   __shared__ int rows_lds[kMaxRowsPerGroup];
   __shared__ int32_t tok_a[kRound], pos_a[kRound];
   __shared__ float alpha_lds[8][At::NHP];
-  const int p = blockIdx.x, kvh = (int)blockIdx.y / a.qg, g = (int)blockIdx.y % a.qg, s = blockIdx.z;
+  // Work item f = p + P * (y + Hkv * qg * s), y = kvh * qg + g.  Workgroup i
+  // of a launch runs on XCD i mod 8, and each XCD has an L2 of its own; the
+  // workgroups of one selecting row read the same selection inputs and
+  // page-table row, so consecutive work items go to one XCD (workgroups
+  // i < 8 * (n / 8) take f = (i mod 8) * (n / 8) + i / 8): a row's workgroups
+  // sit on as few XCDs as the grid allows, and each L2 fetches those inputs
+  // once.  Any numbering is correct; this one only saves reads.
+  const uint32_t nwg = gridDim.x, q8 = nwg >> 3, wi = blockIdx.x;
+  const uint32_t f = (wi < 8u * q8) ? (wi & 7u) * q8 + (wi >> 3) : wi;
+  const uint32_t yn = (uint32_t)(a.Hkv * a.qg), fy = f / (uint32_t)a.P;
+  const int p = (int)(f % (uint32_t)a.P), y = (int)(fy % yn), s = (int)(fy / yn);
+  const int kvh = y / a.qg, g = y % a.qg;
   const int w = threadIdx.x / 64;
   int bv = 0;  // the request id, loaded behind the histogram (vector load, see RowSelector::first)
   int b = 0, Lsel = 0;
@@ -704,7 +715,7 @@ __global__ __launch_bounds__(kFinThreads) void select_decode_kernel(DecodeArgs a
   // the waits for them): row group 0 writes its run of the row's top-k (the
   // last split pads it); workgroup (0, 0) of the row clears its row of the
   // next call's histogram; one workgroup publishes the count.
-  if (blockIdx.y == 0) {
+  if (y == 0) {
     int32_t* trow = topk_out + (size_t)s * a.k;
     for (int i = threadIdx.x; i < ba.n; i += kFinThreads) trow[i0 + i] = list_a[i];
     if (p == a.P - 1)
@@ -926,7 +937,7 @@ qsa_status launch_select_decode(const qsa_config& c, int32_t R, int32_t S, int32
     a.qpw = (qps + a.qg - 1) / a.qg;
     a.nh = a.G * a.qpw;
     const WsPtrs ws = ws_ptrs(lay, ws_base);
-    dim3 grid(P, c.num_kv_heads * a.qg, S);
+    dim3 grid((uint32_t)(P * c.num_kv_heads * a.qg * S));  // < kDecodeWideMaxGroups (checked above)
     const bool fp8 = c.kv_dtype == QSA_KV_FP8_E4M3;
     bool done;
     if (c.head_dim == 128)
