@@ -615,7 +615,8 @@ static_assert(select_decode_ok<128, kFusedHeads128>() && !select_decode_ok<128, 
 // kIdent: no row map (row_sel null; row s is selecting row s, qg = qpw = 1).
 // A template parameter, not a branch: the hook then issues the same loads on
 // every path, and the compiler's waits count exactly the loads before them.
-template <int D, int NH, bool FP8, bool kIdent>
+// KK: list keys per thread in the selection's first round (fused_keys).
+template <int D, int NH, bool FP8, bool kIdent, int KK>
 __global__ __launch_bounds__(kFinThreads) void select_decode_kernel(DecodeArgs a, WsPtrs ws, int32_t max_seq_len,
                                                                      int32_t* __restrict__ topk_out) {
   static_assert(kFinThreads == 8 * 64, "the selection runs on the attention's 8 waves");
@@ -673,7 +674,7 @@ __global__ __launch_bounds__(kFinThreads) void select_decode_kernel(DecodeArgs a
       if (e < nbt) bt_lds[e] = btv[i];
     }
   };
-  sel.first(a.sel_seq_len, max_seq_len, pre, hook, mid);
+  sel.template first<KK>(a.sel_seq_len, max_seq_len, pre, hook, mid);
   // rows_lds and bt_lds were written before the classification's barrier: the
   // query rows of a row map go out now, waited for only at the first tile
   if constexpr (!ident) at.load_q(a, kvh, [&](int i) { return rows_lds[i]; });
@@ -855,12 +856,22 @@ template <int D, int NH, bool FP8>
 bool launch_select_decode_t(dim3 grid, const DecodeArgs& a, const WsPtrs& ws, int32_t max_seq_len,
                             int32_t* topk, hipStream_t stream) {
   if constexpr (select_decode_ok<D, NH>()) {
-    if (a.row_sel == nullptr)
-      hipLaunchKernelGGL((select_decode_kernel<D, NH, FP8, true>), grid, dim3(kFinThreads), 0, stream, a, ws,
-                         max_seq_len, topk);
-    else
-      hipLaunchKernelGGL((select_decode_kernel<D, NH, FP8, false>), grid, dim3(kFinThreads), 0, stream, a, ws,
-                         max_seq_len, topk);
+    const bool k4 = fused_keys(ws.nb_stride) == 4;
+    if (a.row_sel == nullptr) {
+      if (k4)
+        hipLaunchKernelGGL((select_decode_kernel<D, NH, FP8, true, 4>), grid, dim3(kFinThreads), 0, stream, a, ws,
+                           max_seq_len, topk);
+      else
+        hipLaunchKernelGGL((select_decode_kernel<D, NH, FP8, true, kFinKeys>), grid, dim3(kFinThreads), 0, stream,
+                           a, ws, max_seq_len, topk);
+    } else {
+      if (k4)
+        hipLaunchKernelGGL((select_decode_kernel<D, NH, FP8, false, 4>), grid, dim3(kFinThreads), 0, stream, a, ws,
+                           max_seq_len, topk);
+      else
+        hipLaunchKernelGGL((select_decode_kernel<D, NH, FP8, false, kFinKeys>), grid, dim3(kFinThreads), 0, stream,
+                           a, ws, max_seq_len, topk);
+    }
     return true;
   } else {
     return false;

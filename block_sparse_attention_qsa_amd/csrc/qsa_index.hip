@@ -68,11 +68,11 @@ struct AppendArgs {
 // bin is found by one wave walking down from the chunk's highest bin.
 template <int NT, int IT>
 __device__ __forceinline__ void chunk_candidates(const uint32_t* hist, int maxbin, const int32_t (&sc)[IT], int c,
-                                                 int nb, int nb_stride, uint64_t* keys, uint32_t* cinfo,
+                                                 int nb, int list_m, uint64_t* keys, uint32_t* cinfo,
                                                  int32_t* s_lb, uint32_t* s_cnt) {
   const int tid = threadIdx.x, l = lane_id();
   const int valid_total = min(kScoreChunk, nb - c * kScoreChunk);
-  const uint32_t m = (uint32_t)min(local_m(nb_stride), valid_total);
+  const uint32_t m = (uint32_t)min(list_m, valid_total);
   // The local bin, by wave 0 alone: 64 bins at a time downward from the
   // chunk's highest occupied bin (one step, as a rule); the count of all bins
   // is valid_total >= m, so the walk ends before bin 0.
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   // this chunk's candidates for the finalize (no separate filter pass)
   __shared__ int32_t s_lb;
   __shared__ uint32_t s_cnt;
-  chunk_candidates<kScoreThreads, kScoreIters>(hist, s_maxbin, sc, c, nb, ws.nb_stride,
+  chunk_candidates<kScoreThreads, kScoreIters>(hist, s_maxbin, sc, c, nb, ws.list_m,
                                                ws.keys + (size_t)s * ws.nb_stride + (size_t)c * kScoreChunk,
                                                ws.cinfo + (size_t)s * (ws.nb_stride / kScoreChunk) + c,
                                                &s_lb, &s_cnt);
@@ -539,7 +539,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_score_kernel(
   // (chunk_candidates): the local bin of its m-th best valid block, found by
   // wave w for rows w, w + 4, w + 8, w + 12 walking down from the row's
   // highest bin; then every valid block at or above it.
-  const int lm = local_m(ws.nb_stride);
+  const int lm = ws.list_m;
   for (int m = w; m < kPfRows; m += kPfThreads / 64) {
     const int nbr = __shfl(nbc, m, 64);  // lane m holds row r0 + m's length
     const int valid_total = min(kScoreChunk, nbr - c * kScoreChunk);

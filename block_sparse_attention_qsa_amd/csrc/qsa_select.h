@@ -22,6 +22,36 @@ namespace qsa {
 
 namespace {
 
+constexpr int kFinKeys = 8;  // candidate keys per finalize thread and round
+
+// Finalize threads per chunk in a round: as many as share the 512 threads with
+// every chunk of the widest row (one round of loads covers rows of up to 512
+// chunks), at most kScoreChunk / kFinKeys (a round never reads past a chunk's
+// list region).
+__host__ __device__ __forceinline__ int chunk_threads(int nb_stride) {
+  const int nch = nb_stride / kScoreChunk;
+  int t = 1;
+  while (t * 2 * nch <= 512 && t * 2 * kFinKeys <= kScoreChunk) t *= 2;
+  return t;
+}
+// Keys per thread in the fused kernel's first round: 4 where a chunk has at
+// least 16 threads (rows of up to 32 chunks, 131,072 tokens), else kFinKeys.
+__host__ __device__ __forceinline__ int fused_keys(int nb_stride) {
+  return chunk_threads(nb_stride) >= 16 ? 4 : kFinKeys;
+}
+// Each chunk lists at least local_m candidates (with the ties of its last
+// bin): 2 x the threads per chunk where the fused kernel reads 4 keys per
+// thread, else 4 x.  A top-512 takes about tpc blocks from a row's average
+// chunk, so the lists hold 2 or 4 times that, and with the ties they still
+// fit the first round's 4 or 8 keys per thread: at 16 or more threads per
+// chunk the count's spread is small against 2 x its mean; at 8 (rows of
+// 262,144 tokens) a 2 x list sends chunks to the score fallback and a 3 x
+// list with its ties overflows 4 x tpc slots in about a third of the chunks.
+__host__ __device__ __forceinline__ int local_m(int nb_stride) {
+  const int t = chunk_threads(nb_stride);
+  return fused_keys(nb_stride) == 4 ? 2 * t : 4 * t;
+}
+
 struct WsPtrs {
   int32_t* scores;
   uint64_t* keys;
@@ -32,6 +62,7 @@ struct WsPtrs {
   uint32_t* gen;        // [0]: calls scored, [1]: calls selected (see TopkWorkspace)
   size_t hist_stride;
   int32_t nb_stride;
+  int32_t list_m;       // local_m(nb_stride): the scans' candidate-list length
 };
 
 inline WsPtrs ws_ptrs(const TopkWorkspace& lay, void* ws_base) {
@@ -46,6 +77,7 @@ inline WsPtrs ws_ptrs(const TopkWorkspace& lay, void* ws_base) {
   ws.gen = reinterpret_cast<uint32_t*>(base + lay.off_gen);
   ws.hist_stride = (size_t)lay.rows * kBins;
   ws.nb_stride = lay.nb_stride;
+  ws.list_m = local_m(lay.nb_stride);
   return ws;
 }
 
@@ -104,22 +136,6 @@ __device__ __forceinline__ void load_hist_desc(const uint32_t* h, uint32_t (&cnt
 #pragma unroll
   for (int i = 0; i < kPer; ++i) cnt[i] = h[kBins - 1 - (kPer * threadIdx.x + i)];
 }
-
-constexpr int kFinKeys = 8;  // candidate keys per finalize thread and round
-
-// Finalize threads per chunk in a round: as many as share the 512 threads with
-// every chunk of the widest row (one round of loads covers rows of up to 512
-// chunks), at most kScoreChunk / kFinKeys (a round never reads past a chunk's
-// list region).  Each chunk lists at least local_m = 4 x that many candidates,
-// so a row's lists hold about 2,048 candidates whatever its length: about four
-// times the blocks a top-512 takes from the row's average chunk.
-__device__ __forceinline__ int chunk_threads(int nb_stride) {
-  const int nch = nb_stride / kScoreChunk;
-  int t = 1;
-  while (t * 2 * nch <= 512 && t * 2 * kFinKeys <= kScoreChunk) t *= 2;
-  return t;
-}
-__device__ __forceinline__ int local_m(int nb_stride) { return chunk_threads(nb_stride) * 4; }
 
 // The digit of an MSB-first radix select from one pass's 256-bin histogram:
 // lane l owns digits 255-4l .. 252-4l (descending).  Picks the digit holding
@@ -439,11 +455,12 @@ struct RowSelector {
   // length and the count of scored calls are vector loads issued behind the
   // histogram, so that nothing waits for a scalar round trip before the
   // histogram goes out.
-  template <class Pre, class Hook, class Mid>
+  // KK: keys per thread in the first round (fused_keys of the workspace).
+  template <int KK, class Pre, class Hook, class Mid>
   __device__ __forceinline__ void first(const int32_t* __restrict__ sel_seq_len, int32_t max_seq_len, Pre&& pre,
                                         Hook&& hook, Mid&& mid) {
     constexpr int kPer = kBins / kFinThreads;
-    static_assert(kPer == 4 && kFinKeys == 8, "vector loads of the first round");
+    static_assert(kPer == 4 && (KK == 4 || KK == 8), "vector loads of the first round");
     const int tid = threadIdx.x;
     const int nchunks_max = ws.nb_stride / kScoreChunk;
     tpc = chunk_threads(ws.nb_stride);
@@ -456,7 +473,7 @@ struct RowSelector {
 
     // First round, one 16-byte load per four histogram bins or two keys: both
     // histogram rows (bins 2047 - 4 tid - i, i < 4: descending), the chunk's
-    // cinfo and the first kFinKeys keys of its list.
+    // cinfo and the first KK keys of its list.
     const uint4 hv0 = *reinterpret_cast<const uint4*>(ghist0 + kBins - 4 - 4 * tid);
     const uint4 hv1 = *reinterpret_cast<const uint4*>(ghist0 + ws.hist_stride + kBins - 4 - 4 * tid);
     pre();
@@ -464,11 +481,11 @@ struct RowSelector {
     const int32_t tv = vload_same(reinterpret_cast<const int32_t*>(ws.gen));
     int cc = min(tid / tpc, nchunks_max - 1);
     uint32_t ci = cinfo[cc];
-    uint64_t kk[kFinKeys];
+    uint64_t kk[KK];
     auto load_keys = [&](int c) {
-      const i32x4* kp = reinterpret_cast<const i32x4*>(ckeys + (size_t)c * kScoreChunk + sub * kFinKeys);
+      const i32x4* kp = reinterpret_cast<const i32x4*>(ckeys + (size_t)c * kScoreChunk + sub * KK);
 #pragma unroll
-      for (int e = 0; e < kFinKeys / 2; ++e) {
+      for (int e = 0; e < KK / 2; ++e) {
         const i32x4 v = kp[e];
         kk[2 * e] = (uint64_t)(uint32_t)v[0] | ((uint64_t)(uint32_t)v[1] << 32);
         kk[2 * e + 1] = (uint64_t)(uint32_t)v[2] | ((uint64_t)(uint32_t)v[3] << 32);
@@ -504,7 +521,7 @@ struct RowSelector {
     threshold_from_counts<kFinThreads>(hc, ks, L.sh, &L.T, &L.above);
     asm volatile("" ::"v"(ci));
 #pragma unroll
-    for (int e = 0; e < kFinKeys; ++e) asm volatile("" ::"v"(kk[e]));
+    for (int e = 0; e < KK; ++e) asm volatile("" ::"v"(kk[e]));
     T = L.T;
     above = L.above;
 
@@ -529,13 +546,13 @@ struct RowSelector {
         const int lb = (int)(ci & 0xffffu);
         if (lb <= T) {  // the list holds every block of this chunk with bin >= T
 #pragma unroll
-          for (int e = 0; e < kFinKeys; ++e) {
+          for (int e = 0; e < KK; ++e) {
             const int bin = score_bin(key_score(kk[e]));
-            const bool valid = (uint32_t)(sub * kFinKeys + e) < cnt;
+            const bool valid = (uint32_t)(sub * KK + e) < cnt;
             if (valid && bin > T) mark(0xffffffffu - (uint32_t)(kk[e] & 0xffffffffull));
             at_t |= (valid && bin == T) ? 1u << e : 0u;
           }
-          for (uint32_t i = (uint32_t)(tpc * kFinKeys + sub); i < cnt; i += tpc)
+          for (uint32_t i = (uint32_t)(tpc * KK + sub); i < cnt; i += tpc)
             classify(ckeys[(size_t)c * kScoreChunk + i]);
         } else if (sub == 0) {  // local bin above T: bins [T, lb) are not listed
           L.fb[atomicAdd(&L.nfb, 1u)] = (uint16_t)c;
@@ -550,7 +567,7 @@ struct RowSelector {
         base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
         uint32_t pos = base + incl - na;
 #pragma unroll
-        for (int e = 0; e < kFinKeys; ++e) {
+        for (int e = 0; e < KK; ++e) {
           if ((at_t & (1u << e)) && pos < (uint32_t)kCandLds) L.cand[pos] = kk[e];
           pos += (at_t >> e) & 1u;
         }
