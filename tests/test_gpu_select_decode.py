@@ -142,6 +142,23 @@ def test_select_decode_coarse_ties_over_several_chunks():
     _same(a, b)
 
 
+@pytest.mark.parametrize("L", [131072, 131080])
+def test_select_decode_coarse_ties_either_side_of_the_key_count_switch(L):
+    """Rows of up to 131,072 tokens (32 chunks, 16 threads per chunk) take
+    lists of 2 x the threads per chunk and 4 keys per thread in the fused
+    selection's first round; one more block (33 chunks, 8 threads per chunk)
+    switches to lists of 4 x and 8 keys.  Coarse ties put many blocks in each
+    list's last bin, so on both sides lists overflow the first round and
+    chunks go to the score fallback."""
+    wl = make_workload(SHAPE_MAIN, [L, 40001, 5], seed=22, device=DEV, name=f"seldec-switch-{L}")
+    g = torch.Generator(device=DEV).manual_seed(22)
+    wl.keys.copy_(torch.randint(-1, 2, wl.keys.shape, generator=g, device=DEV, dtype=torch.int8))
+    say(f"[gpu] coarse ties at the key-count switch, L={L}")
+    a, b = _pair(wl, 4, launches=1)
+    check_layer(wl, a)
+    _same(a, b)
+
+
 def test_select_decode_repeat_leaves_workspace_clean():
     """Repeated steps give the same results (the histogram and the row
     counters are left clear), and a selecting index call on the same workspace
