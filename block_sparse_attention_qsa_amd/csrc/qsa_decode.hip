@@ -856,21 +856,18 @@ template <int D, int NH, bool FP8>
 bool launch_select_decode_t(dim3 grid, const DecodeArgs& a, const WsPtrs& ws, int32_t max_seq_len,
                             int32_t* topk, hipStream_t stream) {
   if constexpr (select_decode_ok<D, NH>()) {
-    const bool k4 = fused_keys(ws.nb_stride) == 4;
+    const int kk = fused_keys(ws.nb_stride);
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(kFinThreads), 0, stream, a, ws, max_seq_len, topk);
+    };
     if (a.row_sel == nullptr) {
-      if (k4)
-        hipLaunchKernelGGL((select_decode_kernel<D, NH, FP8, true, 4>), grid, dim3(kFinThreads), 0, stream, a, ws,
-                           max_seq_len, topk);
-      else
-        hipLaunchKernelGGL((select_decode_kernel<D, NH, FP8, true, kFinKeys>), grid, dim3(kFinThreads), 0, stream,
-                           a, ws, max_seq_len, topk);
+      if (kk == 4) go(select_decode_kernel<D, NH, FP8, true, 4>);
+      else if (kk == 6) go(select_decode_kernel<D, NH, FP8, true, 6>);
+      else go(select_decode_kernel<D, NH, FP8, true, kFinKeys>);
     } else {
-      if (k4)
-        hipLaunchKernelGGL((select_decode_kernel<D, NH, FP8, false, 4>), grid, dim3(kFinThreads), 0, stream, a, ws,
-                           max_seq_len, topk);
-      else
-        hipLaunchKernelGGL((select_decode_kernel<D, NH, FP8, false, kFinKeys>), grid, dim3(kFinThreads), 0, stream,
-                           a, ws, max_seq_len, topk);
+      if (kk == 4) go(select_decode_kernel<D, NH, FP8, false, 4>);
+      else if (kk == 6) go(select_decode_kernel<D, NH, FP8, false, 6>);
+      else go(select_decode_kernel<D, NH, FP8, false, kFinKeys>);
     }
     return true;
   } else {

@@ -35,21 +35,24 @@ __host__ __device__ __forceinline__ int chunk_threads(int nb_stride) {
   return t;
 }
 // Keys per thread in the fused kernel's first round: 4 where a chunk has at
-// least 16 threads (rows of up to 32 chunks, 131,072 tokens), else kFinKeys.
+// least 16 threads (rows of up to 32 chunks, 131,072 tokens), 6 at 8 threads
+// (up to 64 chunks, 262,144 tokens), else kFinKeys.
 __host__ __device__ __forceinline__ int fused_keys(int nb_stride) {
-  return chunk_threads(nb_stride) >= 16 ? 4 : kFinKeys;
+  const int t = chunk_threads(nb_stride);
+  return t >= 16 ? 4 : (t == 8 ? 6 : kFinKeys);
 }
 // Each chunk lists at least local_m candidates (with the ties of its last
-// bin): 2 x the threads per chunk where the fused kernel reads 4 keys per
-// thread, else 4 x.  A top-512 takes about tpc blocks from a row's average
-// chunk, so the lists hold 2 or 4 times that, and with the ties they still
-// fit the first round's 4 or 8 keys per thread: at 16 or more threads per
-// chunk the count's spread is small against 2 x its mean; at 8 (rows of
-// 262,144 tokens) a 2 x list sends chunks to the score fallback and a 3 x
-// list with its ties overflows 4 x tpc slots in about a third of the chunks.
+// bin): half as many as the first round's keys per thread, times the threads
+// per chunk (tpc).  A top-512 takes about tpc blocks from a row's average
+// chunk, so the lists hold 2, 3 or 4 times that (4, 6 or 8 keys), and with the
+// ties of their last bin they still fit the round: the count's spread is small
+// against 2 x its mean at 16 or more threads per chunk; at 8 (rows of 262,144
+// tokens) a 2 x list sends chunks to the score fallback, and a 3 x list with
+// its ties needs up to 6 keys per thread (it overflows 4 in about a third of
+// the chunks).
 __host__ __device__ __forceinline__ int local_m(int nb_stride) {
   const int t = chunk_threads(nb_stride);
-  return fused_keys(nb_stride) == 4 ? 2 * t : 4 * t;
+  return t * (fused_keys(nb_stride) / 2);
 }
 
 struct WsPtrs {
@@ -460,7 +463,7 @@ struct RowSelector {
   __device__ __forceinline__ void first(const int32_t* __restrict__ sel_seq_len, int32_t max_seq_len, Pre&& pre,
                                         Hook&& hook, Mid&& mid) {
     constexpr int kPer = kBins / kFinThreads;
-    static_assert(kPer == 4 && (KK == 4 || KK == 8), "vector loads of the first round");
+    static_assert(kPer == 4 && (KK == 4 || KK == 6 || KK == 8), "vector loads of the first round");
     const int tid = threadIdx.x;
     const int nchunks_max = ws.nb_stride / kScoreChunk;
     tpc = chunk_threads(ws.nb_stride);

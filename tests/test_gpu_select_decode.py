@@ -147,7 +147,7 @@ def test_select_decode_coarse_ties_either_side_of_the_key_count_switch(L):
     """Rows of up to 131,072 tokens (32 chunks, 16 threads per chunk) take
     lists of 2 x the threads per chunk and 4 keys per thread in the fused
     selection's first round; one more block (33 chunks, 8 threads per chunk)
-    switches to lists of 4 x and 8 keys.  Coarse ties put many blocks in each
+    switches to lists of 3 x and 6 keys.  Coarse ties put many blocks in each
     list's last bin, so on both sides lists overflow the first round and
     chunks go to the score fallback."""
     wl = make_workload(SHAPE_MAIN, [L, 40001, 5], seed=22, device=DEV, name=f"seldec-switch-{L}")
