@@ -11,7 +11,9 @@ fp8, selecting rows whose query rows are spread over several workgroups,
 uneven draft rows per request through row_sel) and the two-launch fallback
 (large grids, one row with more heads than a workgroup holds, slices past
 the LDS bitmap), rows with fewer than k blocks, rows with nothing scored, and
-rows whose threshold bin holds more candidates than the LDS (massive ties).
+rows whose threshold bin holds more candidates than the LDS (massive ties),
+coarse ties on both sides of the selection's key-count switch, and a row
+whose selection clusters in its most recent chunks (score fallback).
 Each case also asserts which of the two paths the library takes.
 """
 import numpy as np
@@ -155,6 +157,29 @@ def test_select_decode_coarse_ties_either_side_of_the_key_count_switch(L):
     wl.keys.copy_(torch.randint(-1, 2, wl.keys.shape, generator=g, device=DEV, dtype=torch.int8))
     say(f"[gpu] coarse ties at the key-count switch, L={L}")
     a, b = _pair(wl, 4, launches=1)
+    check_layer(wl, a)
+    _same(a, b)
+
+
+@pytest.mark.parametrize("L", [100003, 200003])
+def test_select_decode_recent_blocks_cluster(L):
+    """Request 0's most recent 6,000 tokens get keys aligned with its query
+    (random magnitudes, so the scores differ): the top-512 of that row falls
+    in the last one or two chunks, each holding far more selected blocks than
+    its list, so those chunks take the score fallback while the rest of the
+    row has none selected.  Both sides of the key-count switch (25 and 49
+    chunks)."""
+    wl = make_workload(SHAPE_MAIN, [L, 40001, 777], seed=23, device=DEV, name=f"seldec-cluster-{L}")
+    b0 = int(wl.sel_req[0])
+    lo, hi = int(wl.key_off[b0]) + L - 6000, int(wl.key_off[b0]) + L
+    sign = torch.sign(wl.q_index[0].to(torch.int32))
+    g = torch.Generator(device=DEV).manual_seed(23)
+    mag = torch.randint(40, 128, (hi - lo, wl.shape.index_dim), generator=g, device=DEV, dtype=torch.int32)
+    wl.keys[lo:hi] = (sign[None, :] * mag).to(torch.int8)
+    say(f"[gpu] clustered recent blocks, L={L}")
+    a, b = _pair(wl, 4, launches=1)
+    top = a.topk.cpu().numpy()[0]
+    assert (top >= (L - 6000) // 4 - 1).all(), "the row's selection should sit in its recent blocks"
     check_layer(wl, a)
     _same(a, b)
 
