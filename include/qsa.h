@@ -163,6 +163,9 @@ qsa_status qsa_index_topk_workspace_init(void* workspace, size_t ws_bytes, hipSt
  * (score descending, block index ascending) are written to topk[s] (int32 [S, k])
  * in ascending block order, followed by -1.  Rows with L < 4 get all -1.
  * Ties are broken towards the lower block index, so the result is unique.
+ * sel_req[s] must be a row of block_table even for a row with nothing to
+ * select (a dummy row is sel_seq_len[s] = 0 with any valid request id): the
+ * calls read that row's page-table entries.
  *   max_seq_len: host-side bound of sel_seq_len (<= QSA_MAX_SEQ_LEN); it sizes
  *                the grid and the workspace.  Rows longer than it are treated
  *                as max_seq_len long.
