@@ -111,6 +111,21 @@ def test_uneven_draft_rows_through_row_sel(kv):
     assert torch.equal(a.topk, b.topk)
 
 
+@pytest.mark.parametrize("L,kv", [(100003, "bf16"), (200003, "bf16"), (200003, "fp8"), (600003, "fp8")])
+def test_row_map_at_each_key_count(L, kv):
+    """Uneven draft rows through row_sel with the longest row at 100k, 200k and
+    600k tokens: the fused selection's first round then reads 4, 6 and 8 list
+    keys per thread (16, 8 and 2 threads per chunk)."""
+    shape = QSAShape(16, 2, 128, 64, 512, 64, kv_dtype=kv)
+    wl = make_workload(shape, [L, 9001, 5000], rows_per_req=[2, 3, 1], seed=424, device=DEV,
+                       name=f"seldec-rowmap-{L}-{kv}")
+    say(f"[gpu] row map with the longest row at {L} tokens ({kv})")
+    a, b = _pair(wl, 4, launches=1)
+    check_layer(wl, a)
+    check_layer(wl, b)
+    assert torch.equal(a.topk, b.topk)
+
+
 def test_select_decode_large_grid_uses_two_launches():
     """64 selecting rows x 2 KV heads x 4 splits = 512 workgroups: the fallback path."""
     lens = [3000 + 97 * i for i in range(64)]
