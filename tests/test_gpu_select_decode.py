@@ -126,6 +126,18 @@ def test_row_map_at_each_key_count(L, kv):
     assert torch.equal(a.topk, b.topk)
 
 
+@pytest.mark.parametrize("L,kv", [(200003, "bf16"), (600003, "fp8")])
+def test_head_dim_64_at_six_and_eight_keys(L, kv):
+    """d = 64 (16 heads of one KV group per workgroup) with rows long enough
+    for 6 and 8 list keys per thread."""
+    shape = QSAShape(16, 1, 64, 64, 512, 64, kv_dtype=kv)
+    wl = make_workload(shape, [L, 20001, 3], seed=425, device=DEV, name=f"seldec-d64-{L}-{kv}")
+    say(f"[gpu] d=64, longest row {L} tokens ({kv})")
+    a, b = _pair(wl, 3, launches=1)
+    check_layer(wl, a)
+    _same(a, b)
+
+
 def test_select_decode_large_grid_uses_two_launches():
     """64 selecting rows x 2 KV heads x 4 splits = 512 workgroups: the fallback path."""
     lens = [3000 + 97 * i for i in range(64)]
